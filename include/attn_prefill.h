@@ -1,0 +1,125 @@
+/*
+ * attn_prefill.h -- C ABI of the MI355X (gfx950) exact attention-prefill library.
+ *
+ * The operation is exact scaled-dot-product attention over packed
+ * variable-length sequences,
+ *
+ *     out[t, h, :] = sum_{j in J(t)} softmax_j(scale * <q[t, h], k[j, g]>) * v[j, g, :]
+ *
+ * with g = h / (n_q_heads / n_kv_heads).  This is the computation the paper
+ * "A Modern Multimodal Assistant on a 6 GB 2011 GPU" makes fast for long
+ * contexts (abstract, result (iii): the O(N^2) attention of 2k-10k-token
+ * prefill, rewritten without changing its result); its gist.science technical
+ * summary (Metodologia, attention rewrite) names the causal form used by the
+ * language model and the bidirectional form used by the vision tower, and the
+ * abstract names the window-attention merger, the third mask kind here.
+ * Unlike the paper's per-head GEMMs writing an N x N score buffer, one fused
+ * kernel keeps scores on chip; the N x N matrix never exists in memory.
+ *
+ * Visible keys J(t) of the query at local position i of a sequence of n
+ * tokens (positions local to that sequence; sequences never see each other):
+ *   ATTN_CAUSAL   keys 0..i (diagonal included)
+ *   ATTN_FULL     keys 0..n-1 (bidirectional)
+ *   ATTN_WINDOW   the block of `window` tokens holding i, blocks aligned to the
+ *                 sequence start, bidirectional inside; the last block of a
+ *                 sequence may be shorter.
+ *
+ * Layout ("packed THD"): q and out are [T][n_q_heads][head_dim], k and v are
+ * [T][n_kv_heads][head_dim], contiguous row-major, T = cu_seqlens[n_seqs].
+ * All four share one element type (ATTN_BF16 or ATTN_F32).  Device pointers
+ * must be 16-byte aligned.  bf16 inputs are multiplied on matrix cores with
+ * fp32 accumulation and a fp32 softmax; the output is rounded to bf16 (nearest
+ * even).  fp32 inputs are computed in fp32 on the vector ALUs.
+ *
+ * Ownership: the caller owns every buffer.  cu_seqlens is a HOST array read
+ * only during the call.  The library allocates no device memory, holds no
+ * per-call state and may be called from several threads on several streams.
+ *
+ * Execution: stream-ordered and asynchronous.  The call validates its
+ * arguments on the host, enqueues its kernel(s) on `stream` (a hipStream_t;
+ * NULL is the default stream) and returns; `out` is ready when the stream has
+ * reached that point.  Results are deterministic: the same inputs give the
+ * same bits.
+ *
+ * Errors: every argument is checked before any device work; on error nothing
+ * is enqueued and `out` is untouched.  No C++ exception crosses the ABI.
+ */
+#ifndef ATTN_PREFILL_H
+#define ATTN_PREFILL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define ATTN_OK 0
+#define ATTN_EINVAL (-1)      /* bad argument (see attn_prefill) */
+#define ATTN_EUNSUPPORTED (-2) /* valid request this build does not implement */
+#define ATTN_ELAUNCH (-3)      /* the HIP runtime refused the launch */
+
+/* element types */
+#define ATTN_BF16 1
+#define ATTN_F32 2
+
+/* mask kinds */
+#define ATTN_CAUSAL 0
+#define ATTN_FULL 1
+#define ATTN_WINDOW 2
+
+/*
+ * Exact attention prefill over a packed batch.
+ *
+ *   q, k, v      device inputs as laid out above (read only)
+ *   out          device output [T][n_q_heads][head_dim]; must not overlap
+ *                q, k or v
+ *   cu_seqlens   host int32[n_seqs + 1]: cu_seqlens[0] = 0, non-decreasing;
+ *                sequence b is tokens cu_seqlens[b] .. cu_seqlens[b+1]-1.
+ *                Empty sequences are allowed.
+ *   n_seqs       number of sequences, >= 0
+ *   n_q_heads    query heads, > 0, a multiple of n_kv_heads
+ *   n_kv_heads   key/value heads, > 0
+ *   head_dim     64, 72 or 128
+ *   dtype        ATTN_BF16 or ATTN_F32
+ *   mask_kind    ATTN_CAUSAL, ATTN_FULL or ATTN_WINDOW
+ *   window       block length W > 0 when mask_kind is ATTN_WINDOW, else ignored
+ *   scale        logit multiplier, any finite value (usually 1/sqrt(head_dim))
+ *   stream       hipStream_t or NULL
+ *
+ * Returns ATTN_OK; ATTN_EINVAL for a NULL or misaligned pointer (pointers may
+ * be NULL only when T = 0), a bad cu_seqlens, n_seqs < 0, heads <= 0 or
+ * n_q_heads % n_kv_heads != 0, an unknown mask kind, window <= 0 for
+ * ATTN_WINDOW, a non-finite scale, or out overlapping an input;
+ * ATTN_EUNSUPPORTED for another head_dim or dtype, or sizes whose element
+ * offsets do not fit in 63 bits; ATTN_ELAUNCH when the runtime reports a
+ * launch failure.  T = 0 succeeds without device work.
+ */
+int attn_prefill(const void *q, const void *k, const void *v, void *out,
+                 const int32_t *cu_seqlens, int32_t n_seqs, int32_t n_q_heads,
+                 int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                 int32_t mask_kind, int32_t window, float scale, void *stream);
+
+/*
+ * The argument checks of attn_prefill alone: same arguments, same status
+ * codes, but host-only -- it touches no device and no pointed-to device
+ * memory, so it can run where there is no GPU.  Returns what attn_prefill
+ * would return before enqueuing anything (ATTN_OK if it would launch).
+ */
+int attn_prefill_check(const void *q, const void *k, const void *v,
+                       const void *out, const int32_t *cu_seqlens,
+                       int32_t n_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                       int32_t head_dim, int32_t dtype, int32_t mask_kind,
+                       int32_t window, float scale);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *attn_strerror(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_PREFILL_H */

@@ -1,0 +1,156 @@
+"""Exact attention prefill for AMD MI355X (gfx950): thin Python binding.
+
+The work is done by ``libattn_prefill.so`` (HIP kernels behind a C ABI, see
+include/attn_prefill.h); this module only marshals torch tensors to it.  The
+functions carry the C entry points' names:
+
+* ``attn_prefill(q, k, v, cu_seqlens, mask="causal", scale=None, out=None)``
+* ``attn_prefill_check(...)``, ``attn_strerror(status)``, ``attn_version()``
+
+There is no fallback: if the library is missing or cannot be loaded, the
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["attn_prefill", "attn_prefill_check", "attn_strerror", "attn_version",
+           "AttnError", "library_path", "load_library", "ATTN_OK", "ATTN_EINVAL",
+           "ATTN_EUNSUPPORTED", "ATTN_ELAUNCH", "ATTN_BF16", "ATTN_F32", "ATTN_CAUSAL",
+           "ATTN_FULL", "ATTN_WINDOW"]
+
+# values of include/attn_prefill.h
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ELAUNCH = 0, -1, -2, -3
+ATTN_BF16, ATTN_F32 = 1, 2
+ATTN_CAUSAL, ATTN_FULL, ATTN_WINDOW = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str = "attn_prefill"):
+        self.status = status
+        super().__init__(f"{what} failed: {attn_strerror(status)} (status {status})")
+
+
+def library_path() -> str:
+    return os.environ.get("ATTN_PREFILL_LIBRARY", os.path.join(_HERE, "libattn_prefill.so"))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the HIP library (after torch, so both share one HIP runtime)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    import torch  # noqa: F401  -- binds libamdhip64 before the library does
+
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m long_context_attention_prefill_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.attn_prefill.argtypes = [vp, vp, vp, vp, ip, i32, i32, i32, i32, i32, i32, i32,
+                                 ctypes.c_float, vp]
+    lib.attn_prefill.restype = ctypes.c_int
+    lib.attn_prefill_check.argtypes = [vp, vp, vp, vp, ip, i32, i32, i32, i32, i32, i32, i32,
+                                       ctypes.c_float]
+    lib.attn_prefill_check.restype = ctypes.c_int
+    lib.attn_strerror.argtypes = [ctypes.c_int]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def attn_strerror(status: int) -> str:
+    return load_library().attn_strerror(int(status)).decode()
+
+
+def attn_version() -> int:
+    return int(load_library().attn_version())
+
+
+def _mask_args(mask):
+    if mask == "causal":
+        return ATTN_CAUSAL, 0
+    if mask == "full":
+        return ATTN_FULL, 0
+    if isinstance(mask, (tuple, list)) and len(mask) == 2 and mask[0] == "window":
+        return ATTN_WINDOW, int(mask[1])
+    raise ValueError(f"mask must be 'causal', 'full' or ('window', W), not {mask!r}")
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _cu_array(cu_seqlens):
+    vals = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+    arr = (ctypes.c_int32 * max(len(vals), 1))(*vals)
+    return arr, len(vals) - 1
+
+
+def _args(q, k, v, out, cu_seqlens, mask, scale):
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [T, Hq, d]; k and v [T, Hkv, d]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2]:
+        raise ValueError("q, k, v shapes disagree")
+    if out.shape != q.shape or out.dtype != q.dtype or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v and out must share dtype; out must have q's shape")
+    kind, window = _mask_args(mask)
+    d = int(q.shape[2])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    cu, n_seqs = _cu_array(cu_seqlens)
+    if n_seqs >= 0 and int(cu[n_seqs]) != q.shape[0]:
+        raise ValueError("cu_seqlens[-1] must equal the number of packed tokens")
+    return (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cu, n_seqs,
+            int(q.shape[1]), int(k.shape[1]), d, _dtype_code(q), kind, window, float(scale))
+
+
+def attn_prefill(q, k, v, cu_seqlens, mask="causal", scale=None, out=None, stream=None):
+    """Exact attention over a packed batch; returns ``out`` ([T, Hq, d], q's dtype).
+
+    q: [T, Hq, d], k/v: [T, Hkv, d] contiguous device tensors (bf16 or fp32);
+    cu_seqlens: host sequence of n_seqs+1 ints; mask: "causal", "full" or
+    ("window", W); scale defaults to 1/sqrt(d).  Runs on ``stream`` (default:
+    torch's current stream) and returns without synchronising.
+    """
+    import torch
+
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    a = _args(q, k, v, out, cu_seqlens, mask, scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream or 0)
+    status = lib.attn_prefill(*a, ctypes.c_void_p(handle))
+    if status != ATTN_OK:
+        raise AttnError(status)
+    return out
+
+
+def attn_prefill_check(q, k, v, cu_seqlens, mask="causal", scale=None, out=None) -> int:
+    """Status attn_prefill would return for these arguments (host-only)."""
+    import torch
+
+    if out is None:
+        out = torch.empty_like(q)
+    a = _args(q, k, v, out, cu_seqlens, mask, scale)
+    return int(load_library().attn_prefill_check(*a))

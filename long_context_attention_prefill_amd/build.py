@@ -1,0 +1,57 @@
+"""Build the HIP library in-tree: ``python -m long_context_attention_prefill_amd.build``.
+
+Produces ``long_context_attention_prefill_amd/libattn_prefill.so`` for gfx950:
+the kernels (csrc/attn_fwd.hip) compiled by hipcc, the host-only C ABI
+(csrc/attn_api.cpp) compiled by g++, linked by hipcc.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+ROOT = os.path.dirname(PKG)
+LIBRARY = os.path.join(PKG, "libattn_prefill.so")
+ARCH = "gfx950"
+
+# Packed-fp32 VALU forms are kept out of every kernel on purpose.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = False, output: str = LIBRARY, extra_device_flags=()) -> str:
+    hipcc = _hipcc()
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    with tempfile.TemporaryDirectory() as tmp:
+        api_o = os.path.join(tmp, "attn_api.o")
+        fwd_o = os.path.join(tmp, "attn_fwd.o")
+        _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", *inc, "-c",
+              os.path.join(CSRC, "attn_api.cpp"), "-o", api_o], verbose)
+        _run([hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", *DEVICE_FLAGS,
+              *extra_device_flags, *inc, "-c", os.path.join(CSRC, "attn_fwd.hip"), "-o", fwd_o],
+             verbose)
+        tmp_out = output + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_out, fwd_o, api_o],
+             verbose)
+        os.replace(tmp_out, output)
+    return output
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,592 @@
+// attn_fwd.hip -- fused exact attention-prefill kernels for gfx950 (MI355X).
+//
+// One pass per (sequence, query head, tile of query rows): K and V tiles are
+// streamed through LDS, scores live only in registers, and an online softmax
+// carries the running maximum and sum, so the N x N score matrix never
+// touches memory.  This replaces the per-head GEMMs into an N x N score
+// buffer that the paper "A Modern Multimodal Assistant on a 6 GB 2011 GPU"
+// uses on Fermi (abstract, result (iii); gist.science technical summary,
+// Metodologia, attention rewrite); the result is the same exact attention.
+//
+// bf16 family: QK^T and PV on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+// Scores are computed transposed, S^T = K Q^T, so each lane owns one query
+// column and 16 keys of each 32x32 block: the row max and row sum are mostly
+// in-lane, and the probabilities already sit in the B-operand layout of
+// O^T = V^T P^T.  V is transposed on its way into LDS (4 keys packed per
+// 8-byte store, XOR-swizzled rows) so PV operands are plain 16-byte reads.
+//
+// fp32 family: vector-ALU kernel, two lanes per query row, K/V tiles in LDS.
+//
+// Visible keys of local row i (sequence of n tokens) form one interval
+// [lo(i), hi(i)) for all three masks, computed with integers only:
+//   causal [0, i+1)   full [0, n)   window [W*floor(i/W), min(W*floor(i/W)+W, n))
+// lo and hi never decrease with i, so a tile of rows sees the union
+// [lo(first), hi(last)) and every row sees the intersection
+// [lo(last), hi(first)); only key tiles not inside the intersection are
+// masked element by element, and tiles outside the union are never loaded.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_launch.h"
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Softmax runs in base 2 on scores pre-multiplied by scale*log2(e).  The
+// reference maximum is raised only when a row's new maximum exceeds it by
+// more than this many doublings, so probabilities stay below 2^8 and the
+// output/sum rescale is skipped on most tiles.
+constexpr float kRescaleSlack = 8.0f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct Item {
+  int seq;
+  int tile;
+  int head;
+};
+
+// Workgroup r -> (sequence, query tile, query head), heaviest work first.
+// Causal: tile m costs ~(m+1) key tiles in every sequence, so items are
+// ordered by m descending across the batch; otherwise by sequence length
+// (sequences arrive longest first).  The hq heads of one (sequence, tile)
+// are consecutive, and when hq is a multiple of 8 slot s maps to head
+// (s % 8) * (hq / 8) + s / 8: consecutive workgroups land on different XCDs
+// round-robin, so each XCD keeps to a contiguous block of query heads, i.e.
+// to few key/value heads, and their K/V stays in that XCD's L2.
+__device__ Item decode_item(const LaunchArgs &a, int r) {
+  Item it{0, 0, 0};
+  int slot = 0;
+  if (a.mask_kind == kCausal) {
+    int ptr = 0;
+    for (int m = a.seq_tiles[0] - 1; m >= 0; --m) {
+      while (ptr < a.n_seqs && a.seq_tiles[ptr] > m) ++ptr;
+      const int cnt = ptr * a.hq;
+      if (r < cnt) {
+        it.seq = r / a.hq;
+        it.tile = m;
+        slot = r - it.seq * a.hq;
+        break;
+      }
+      r -= cnt;
+    }
+  } else {
+    for (int b = 0; b < a.n_seqs; ++b) {
+      const int cnt = a.seq_tiles[b] * a.hq;
+      if (r < cnt) {
+        it.seq = b;
+        it.tile = r / a.hq;
+        slot = r - it.tile * a.hq;
+        break;
+      }
+      r -= cnt;
+    }
+  }
+  it.head = (a.hq % 8 == 0) ? (slot & 7) * (a.hq >> 3) + (slot >> 3) : slot;
+  return it;
+}
+
+__device__ __forceinline__ void row_range(int mask, int W, int i, int n, int &lo, int &hi) {
+  if (mask == kCausal) {
+    lo = 0;
+    hi = i + 1;
+  } else if (mask == kFull) {
+    lo = 0;
+    hi = n;
+  } else {
+    lo = (i / W) * W;
+    hi = min(lo + W, n);
+  }
+}
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+// ---------------------------------------------------------------------------
+// bf16 / MFMA family
+// ---------------------------------------------------------------------------
+
+// Position of key group kg (4 keys) inside a 16-key chunk of a V^T row.  The
+// S^T accumulator gives lane half g the keys {4g..4g+3, 8+4g..8+4g+3} of
+// each 16; storing key groups in the order 0, 2, 1, 3 makes those 8 keys
+// contiguous, so one 16-byte read yields the A operand of O^T = V^T P^T.
+__device__ __forceinline__ int vt_pos(int kg) {
+  return ((kg >> 2) << 4) | ((kg & 1) << 3) | ((kg & 2) << 1);
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_bf16(const LaunchArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int BM = NW * 32;            // query rows per workgroup
+  constexpr int BN = 64;                 // keys per tile
+  constexpr int DK = (D + 15) / 16 * 16; // head dim padded to the MFMA K step
+  constexpr int KSTEPS = DK / 16;
+  constexpr int DV = (D + 31) / 32 * 32; // head dim padded to 32-row output blocks
+  constexpr int DBLK = DV / 32;
+  constexpr int CH = D / 8;              // 16-byte chunks per row in memory
+  constexpr int KROW = DK + 8;           // bf16 per K row in LDS (16 B pad)
+  constexpr int VROW_DW = (BN + 8) / 2;  // dwords per V^T row in LDS (16 B pad)
+  constexpr int KBUF = BN * KROW;        // bf16 per K buffer
+  constexpr int VBUF_DW = DV * VROW_DW;  // dwords per V^T buffer
+  constexpr int KUNITS = BN * CH;
+  constexpr int VUNITS = (BN / 4) * CH;
+  constexpr int KLOADS = (KUNITS + NT - 1) / NT;
+  constexpr int VLOADS = (VUNITS + NT - 1) / NT;
+  static_assert(BN == 64, "V^T swizzle assumes 8 chunks of 8 keys per row");
+
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2 * KBUF];
+  __shared__ __attribute__((aligned(16))) uint32_t vt_lds[2 * VBUF_DW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  const Item it = decode_item(a, blockIdx.x);
+  const int s0 = a.seq_start[it.seq];
+  const int n = a.seq_len[it.seq];
+  const int h = it.head;
+  const int hk = h / a.group;
+  const int mask = a.mask_kind;
+  const int W = a.window;
+  const float c = a.c;
+  const bool neg = c < 0.0f;
+  const float cabs = neg ? -c : c;
+
+  const int q0 = it.tile * BM;
+  const int qend = min(q0 + BM, n);
+  int kv_lo, kv_hi, tmp;
+  row_range(mask, W, q0, n, kv_lo, tmp);
+  row_range(mask, W, qend - 1, n, tmp, kv_hi);
+
+  const int wq0 = q0 + wave * 32;
+  const bool wave_active = wq0 < n;
+  int w_lo = 0, w_hi = 0, i_lo = 0, i_hi = 0;
+  if (wave_active) {
+    const int wq1 = min(wq0 + 32, n);
+    row_range(mask, W, wq0, n, w_lo, i_hi);
+    row_range(mask, W, wq1 - 1, n, i_lo, w_hi);
+  }
+  const int row = wq0 + l32;
+  const bool row_ok = row < n;
+  int lo_r = 0, hi_r = 0;
+  if (row_ok) row_range(mask, W, row, n, lo_r, hi_r);
+
+  // head-dim padding is read by the MFMAs and must hold zeros
+  if constexpr (DK != D) {
+    for (int u = tid; u < 2 * BN; u += NT) {
+      __bf16 *p = k_lds + u * KROW + D;
+#pragma unroll
+      for (int e = 0; e < DK - D; ++e) p[e] = (__bf16)0.0f;
+    }
+  }
+  if constexpr (DV != D) {
+    for (int u = tid; u < 2 * (DV - D) * VROW_DW; u += NT) {
+      const int b = u / ((DV - D) * VROW_DW);
+      const int r = u - b * (DV - D) * VROW_DW;
+      vt_lds[b * VBUF_DW + D * VROW_DW + r] = 0u;
+    }
+  }
+
+  // Q fragments: the B operand of S^T = K Q^T, lane (l32, g) holds
+  // q[row][16*kk + 8*g .. +7].
+  bf16x8 qf[KSTEPS];
+  {
+    const __bf16 *qrow = reinterpret_cast<const __bf16 *>(a.q) +
+                         ((size_t)(s0 + (row_ok ? row : 0)) * a.hq + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const int d0 = 16 * kk + 8 * g;
+      if (row_ok && d0 < D)
+        qf[kk] = *reinterpret_cast<const bf16x8 *>(qrow + d0);
+      else
+        qf[kk] = (bf16x8)((__bf16)0.0f);
+    }
+  }
+
+  const size_t kv_rs = (size_t)a.hkv * D;  // elements between consecutive tokens
+  const __bf16 *kbase = reinterpret_cast<const __bf16 *>(a.k) + (size_t)s0 * kv_rs + (size_t)hk * D;
+  const __bf16 *vbase = reinterpret_cast<const __bf16 *>(a.v) + (size_t)s0 * kv_rs + (size_t)hk * D;
+
+  u32x4 kreg[KLOADS];
+  u32x4 vreg[VLOADS][4];
+
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int r = 0; r < KLOADS; ++r) {
+      const int u = tid + r * NT;
+      kreg[r] = (u32x4)(0u);
+      if (u < KUNITS) {
+        const int key = u / CH, ch = u - (u / CH) * CH;
+        const int j = kt + key;
+        if (j < kv_hi) kreg[r] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)j * kv_rs + ch * 8);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < VLOADS; ++r) {
+      const int u = tid + r * NT;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) vreg[r][rr] = (u32x4)(0u);
+      if (u < VUNITS) {
+        const int kg = u / CH, dg = u - (u / CH) * CH;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int j = kt + 4 * kg + rr;
+          if (j < kv_hi)
+            vreg[r][rr] = *reinterpret_cast<const u32x4 *>(vbase + (size_t)j * kv_rs + dg * 8);
+        }
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    __bf16 *kb = k_lds + buf * KBUF;
+#pragma unroll
+    for (int r = 0; r < KLOADS; ++r) {
+      const int u = tid + r * NT;
+      if (u < KUNITS) {
+        const int key = u / CH, ch = u - (u / CH) * CH;
+        *reinterpret_cast<u32x4 *>(kb + key * KROW + ch * 8) = kreg[r];
+      }
+    }
+    uint32_t *vb = vt_lds + buf * VBUF_DW;
+#pragma unroll
+    for (int r = 0; r < VLOADS; ++r) {
+      const int u = tid + r * NT;
+      if (u < VUNITS) {
+        const int kg = u / CH, dg = u - (u / CH) * CH;
+        const int pos = vt_pos(kg);
+        const int chunk = pos >> 3, half = (pos >> 2) & 1;
+        const int col = 4 * (chunk ^ (dg & 7)) + 2 * half;  // row d = 8*dg + e: (d >> 3) & 7 == dg & 7
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t a0 = vreg[r][0][p], a1 = vreg[r][1][p];
+          const uint32_t a2 = vreg[r][2][p], a3 = vreg[r][3][p];
+          u32x2 lo, hi;  // d = 8*dg + 2p (low halves) and 8*dg + 2p + 1 (high halves)
+          lo[0] = (a0 & 0xffffu) | (a1 << 16);
+          lo[1] = (a2 & 0xffffu) | (a3 << 16);
+          hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+          hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+          const int d = 8 * dg + 2 * p;
+          *reinterpret_cast<u32x2 *>(vb + d * VROW_DW + col) = lo;
+          *reinterpret_cast<u32x2 *>(vb + (d + 1) * VROW_DW + col) = hi;
+        }
+      }
+    }
+  };
+
+  f32x16 o[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) o[db] = (f32x16)(0.0f);
+  float m_run = row_ok ? kNegInf : 0.0f;  // reference maximum, exp2 units
+  float l_run = 0.0f;                     // this lane's share of the row sum
+
+  auto compute = [&](int kt, int buf) {
+    const bool need_mask = kt < i_lo || kt + BN > i_hi;
+    const __bf16 *kb = k_lds + buf * KBUF;
+    f32x16 s[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      s[nb] = (f32x16)(0.0f);
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8 *>(kb + (nb * 32 + l32) * KROW + 16 * kk + 8 * g);
+        s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[nb], 0, 0, 0);
+      }
+    }
+    // row maximum of this tile (sign folded in: max of c*s), exp2 units
+    float mx = kNegInf;
+    bool any = true;
+    if (!need_mask) {
+      if (neg) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, -s[nb][j]);
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[nb][j]);
+      }
+    } else {
+      any = row_ok && kt < hi_r && kt + BN > lo_r;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = kt + nb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+          const bool vis = key >= lo_r && key < hi_r;
+          const float sv = neg ? -s[nb][j] : s[nb][j];
+          mx = vis ? fmaxf(mx, sv) : mx;
+        }
+    }
+    float mt = any ? mx * cabs : kNegInf;
+    mt = fmaxf(mt, xor32(mt));
+    const bool raise = mt > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float m_new = raise ? mt : m_run;
+      const float alpha = raise ? fast_exp2(m_run - m_new) : 1.0f;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = -m_run;
+    float lsum = 0.0f;
+    if (!need_mask) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float p = fast_exp2(__builtin_fmaf(s[nb][j], c, neg_m));
+          s[nb][j] = p;
+          lsum += p;
+        }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = kt + nb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+          const bool vis = key >= lo_r && key < hi_r;
+          const float p = vis ? fast_exp2(__builtin_fmaf(s[nb][j], c, neg_m)) : 0.0f;
+          s[nb][j] = p;
+          lsum += p;
+        }
+    }
+    l_run += lsum;
+    // P^T fragments (B operand of O^T = V^T P^T): k step ks covers keys
+    // 16ks .. 16ks+15 of the tile, i.e. accumulator entries 8*(ks&1)..+7 of
+    // block ks>>1.
+    bf16x8 pf[BN / 16];
+#pragma unroll
+    for (int ks = 0; ks < BN / 16; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)s[ks >> 1][8 * (ks & 1) + e];
+    const uint32_t *vb = vt_lds + buf * VBUF_DW;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const int d = 32 * db + l32;
+      const int sw = (d >> 3) & 7;
+#pragma unroll
+      for (int ks = 0; ks < BN / 16; ++ks) {
+        const bf16x8 vf =
+            *reinterpret_cast<const bf16x8 *>(vb + d * VROW_DW + 4 * ((2 * ks + g) ^ sw));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
+      }
+    }
+  };
+
+  const int ntiles = (kv_hi - kv_lo + BN - 1) / BN;
+  load_tile(kv_lo);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int kt = kv_lo + t * BN;
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile(kt + BN);
+    if (wave_active && kt < w_hi && kt + BN > w_lo) compute(kt, t & 1);
+    if (more) store_tile((t + 1) & 1);
+    __syncthreads();
+  }
+
+  if (wave_active) {
+    const float l_tot = l_run + xor32(l_run);
+    if (row_ok) {
+      const float inv = 1.0f / l_tot;
+      __bf16 *orow = reinterpret_cast<__bf16 *>(a.out) + ((size_t)(s0 + row) * a.hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d = 32 * db + 8 * jj + 4 * g;
+          if (d < D) {
+            bf16x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * jj + e] * inv);
+            *reinterpret_cast<bf16x4 *>(orow + d) = w;
+          }
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 / vector-ALU family
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void fwd_f32(const LaunchArgs a) {
+  constexpr int NT = 256;
+  constexpr int BM = NT / 2;  // two lanes per query row
+  constexpr int BN = 32;
+  constexpr int DH = D / 2;   // elements per lane
+  constexpr int HROW = DH + 4;  // the two halves of a row sit in different banks
+  constexpr int ROW = 2 * HROW;
+  constexpr int F4 = D / 4;
+  static_assert(DH % 4 == 0, "half rows must be float4 aligned");
+
+  __shared__ __attribute__((aligned(16))) float k_lds[BN * ROW];
+  __shared__ __attribute__((aligned(16))) float v_lds[BN * ROW];
+
+  const int tid = threadIdx.x;
+  const int half = tid & 1;
+  const Item it = decode_item(a, blockIdx.x);
+  const int s0 = a.seq_start[it.seq];
+  const int n = a.seq_len[it.seq];
+  const int h = it.head;
+  const int hk = h / a.group;
+  const int mask = a.mask_kind;
+  const int W = a.window;
+  const float c = a.c;
+
+  const int q0 = it.tile * BM;
+  const int qend = min(q0 + BM, n);
+  int kv_lo, kv_hi, tmp;
+  row_range(mask, W, q0, n, kv_lo, tmp);
+  row_range(mask, W, qend - 1, n, tmp, kv_hi);
+
+  const int row = q0 + (tid >> 1);
+  const bool row_ok = row < n;
+  int lo_r = 0, hi_r = 0;
+  if (row_ok) row_range(mask, W, row, n, lo_r, hi_r);
+
+  float qv[DH], o[DH];
+  {
+    const float *qrow = reinterpret_cast<const float *>(a.q) +
+                        ((size_t)(s0 + (row_ok ? row : 0)) * a.hq + h) * D + half * DH;
+#pragma unroll
+    for (int e = 0; e < DH; e += 4) {
+      f32x4 x = row_ok ? *reinterpret_cast<const f32x4 *>(qrow + e) : (f32x4)(0.0f);
+      qv[e] = x[0];
+      qv[e + 1] = x[1];
+      qv[e + 2] = x[2];
+      qv[e + 3] = x[3];
+    }
+#pragma unroll
+    for (int e = 0; e < DH; ++e) o[e] = 0.0f;
+  }
+  float m_run = kNegInf, l_run = 0.0f;
+
+  const size_t kv_rs = (size_t)a.hkv * D;
+  const float *kbase = reinterpret_cast<const float *>(a.k) + (size_t)s0 * kv_rs + (size_t)hk * D;
+  const float *vbase = reinterpret_cast<const float *>(a.v) + (size_t)s0 * kv_rs + (size_t)hk * D;
+
+  for (int kt = kv_lo; kt < kv_hi; kt += BN) {
+    __syncthreads();  // previous tile fully consumed
+    for (int u = tid; u < BN * F4; u += NT) {
+      const int key = u / F4, col = (u - key * F4) * 4;
+      const int j = kt + key;
+      f32x4 kx = (f32x4)(0.0f), vx = (f32x4)(0.0f);
+      if (j < kv_hi) {
+        kx = *reinterpret_cast<const f32x4 *>(kbase + (size_t)j * kv_rs + col);
+        vx = *reinterpret_cast<const f32x4 *>(vbase + (size_t)j * kv_rs + col);
+      }
+      const int hh = col / DH, cc = col - hh * DH;
+      *reinterpret_cast<f32x4 *>(k_lds + key * ROW + hh * HROW + cc) = kx;
+      *reinterpret_cast<f32x4 *>(v_lds + key * ROW + hh * HROW + cc) = vx;
+    }
+    __syncthreads();
+
+    float x[BN];
+    float mt = kNegInf;
+#pragma unroll
+    for (int jj = 0; jj < BN; ++jj) {
+      const float *kr = k_lds + jj * ROW + half * HROW;
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < DH; e += 4) {
+        const f32x4 kx = *reinterpret_cast<const f32x4 *>(kr + e);
+        acc = __builtin_fmaf(qv[e], kx[0], acc);
+        acc = __builtin_fmaf(qv[e + 1], kx[1], acc);
+        acc = __builtin_fmaf(qv[e + 2], kx[2], acc);
+        acc = __builtin_fmaf(qv[e + 3], kx[3], acc);
+      }
+      acc += __shfl_xor(acc, 1);
+      const int key = kt + jj;
+      const bool vis = row_ok && key >= lo_r && key < hi_r;
+      x[jj] = vis ? acc * c : kNegInf;
+      mt = fmaxf(mt, x[jj]);
+    }
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_run - m_new);
+#pragma unroll
+    for (int e = 0; e < DH; ++e) o[e] *= alpha;
+    l_run *= alpha;
+#pragma unroll
+    for (int jj = 0; jj < BN; ++jj) {
+      const float p = (x[jj] == kNegInf) ? 0.0f : fast_exp2(x[jj] - m_new);
+      l_run += p;
+      const float *vr = v_lds + jj * ROW + half * HROW;
+#pragma unroll
+      for (int e = 0; e < DH; e += 4) {
+        const f32x4 vx = *reinterpret_cast<const f32x4 *>(vr + e);
+        o[e] = __builtin_fmaf(p, vx[0], o[e]);
+        o[e + 1] = __builtin_fmaf(p, vx[1], o[e + 1]);
+        o[e + 2] = __builtin_fmaf(p, vx[2], o[e + 2]);
+        o[e + 3] = __builtin_fmaf(p, vx[3], o[e + 3]);
+      }
+    }
+    m_run = m_new;
+  }
+
+  if (row_ok) {
+    const float inv = 1.0f / l_run;
+    float *orow = reinterpret_cast<float *>(a.out) + ((size_t)(s0 + row) * a.hq + h) * D + half * DH;
+#pragma unroll
+    for (int e = 0; e < DH; e += 4) {
+      f32x4 w;
+      w[0] = o[e] * inv;
+      w[1] = o[e + 1] * inv;
+      w[2] = o[e + 2] * inv;
+      w[3] = o[e + 3] * inv;
+      *reinterpret_cast<f32x4 *>(orow + e) = w;
+    }
+  }
+}
+
+template <typename K>
+int launch(K kernel, const LaunchArgs &a, int threads, void *stream) {
+  void *args[] = {const_cast<LaunchArgs *>(&a)};
+  return static_cast<int>(hipLaunchKernel(reinterpret_cast<const void *>(kernel),
+                                          dim3(a.total_items), dim3(threads), args, 0,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+constexpr int kWavesBf16 = 4;
+
+}  // namespace
+
+int rows_per_workgroup_bf16(int) { return kWavesBf16 * 32; }
+int rows_per_workgroup_f32(int) { return 128; }
+
+int launch_bf16(const LaunchArgs &a, int head_dim, void *stream) {
+  switch (head_dim) {
+    case 64: return launch(fwd_bf16<64, kWavesBf16>, a, kWavesBf16 * 64, stream);
+    case 72: return launch(fwd_bf16<72, kWavesBf16>, a, kWavesBf16 * 64, stream);
+    case 128: return launch(fwd_bf16<128, kWavesBf16>, a, kWavesBf16 * 64, stream);
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
+}
+
+int launch_f32(const LaunchArgs &a, int head_dim, void *stream) {
+  switch (head_dim) {
+    case 64: return launch(fwd_f32<64>, a, 256, stream);
+    case 72: return launch(fwd_f32<72>, a, 256, stream);
+    case 128: return launch(fwd_f32<128>, a, 256, stream);
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
+}
+
+}  // namespace attn

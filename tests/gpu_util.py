@@ -1,0 +1,42 @@
+"""Helpers for GPU tests: move exact-valued float64 arrays to the device in the
+kernel's dtype, call the HIP library through its binding, bring results back."""
+from __future__ import annotations
+
+import numpy as np
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def torch_dtype(dtype):
+    import torch
+
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+
+
+def to_device(x, dtype):
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(torch_dtype(dtype))
+    # inputs already hold dtype values: the conversion must be exact
+    assert np.array_equal(t.double().numpy(), x), "input not exactly representable"
+    return t.to("cuda")
+
+
+def run_hip(q, k, v, cu, mask, scale, dtype, out=None):
+    import torch
+
+    import long_context_attention_prefill_amd as lcap
+
+    tq, tk, tv = to_device(q, dtype), to_device(k, dtype), to_device(v, dtype)
+    res = lcap.attn_prefill(tq, tk, tv, [int(x) for x in cu], mask=mask, scale=scale, out=out)
+    torch.cuda.synchronize()
+    return res.double().cpu().numpy()
+
+
+def max_err(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.size == 0:
+        return 0.0
+    assert np.all(np.isfinite(a)), "non-finite GPU output"
+    return float(np.max(np.abs(a - b)))
