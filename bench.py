@@ -1,0 +1,243 @@
+"""Attention-prefill bench on one MI355X.
+
+A step is one ``attn_prefill`` call (the whole fused path: planning, K/V
+streaming, QK^T, mask, online softmax, PV, epilogue) over one batch of seeded
+synthetic input already resident in HBM.  The headline workload is causal
+bf16 prefill of one 10240-token sequence, 16 query / 2 KV heads, head dim
+128, with the needle planted at 60 % depth; the 2048-token causal case
+(16/16 heads) is timed beside it.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--sweep]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "long_context_attention_prefill_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_d128_causal_n10240.txt")
+
+
+def pairs_of(w):
+    """Unmasked (query, key) pairs per head, from the mask definitions."""
+    total = 0
+    for n in w.seq_lens:
+        if w.mask == "causal":
+            total += n * (n + 1) // 2
+        elif w.mask == "full":
+            total += n * n
+        else:
+            W = w.mask[1]
+            full, rem = divmod(n, W)
+            total += full * W * W + rem * rem
+    return total
+
+
+def algorithmic(w):
+    """(flops, bytes) of one call: 4*d*Hq per pair; Q, K, V read and O written once."""
+    pairs = pairs_of(w)
+    flops = 4 * w.head_dim * w.n_q_heads * pairs
+    es = 2 if w.dtype == "bf16" else 4
+    T = w.total_tokens
+    byts = es * T * w.head_dim * (2 * w.n_q_heads + 2 * w.n_kv_heads)
+    return flops, byts
+
+
+def device_inputs(w):
+    import torch
+
+    from long_context_attention_prefill_amd import workloads as W
+
+    q, k, v, cu = W.make_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = [torch.from_numpy(x).to(dt).to("cuda") for x in (q, k, v)]
+    return (q, k, v, cu), dev
+
+
+def time_calls(w, dev, cu, steps, warmup):
+    """Mean ms per call over `steps` back-to-back calls between two events on
+    the stream the kernels are launched on."""
+    import torch
+
+    import long_context_attention_prefill_amd as lcap
+
+    q, k, v = dev
+    out = torch.empty_like(q)
+    cu_l = [int(x) for x in cu]
+    for _ in range(warmup):
+        lcap.attn_prefill(q, k, v, cu_l, mask=w.mask, scale=w.scale, out=out)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        lcap.attn_prefill(q, k, v, cu_l, mask=w.mask, scale=w.scale, out=out)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, out
+
+
+def kernel_digest():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when that summary is missing or was taken on other kernel source."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("kernel_source_sha256_16") != kernel_digest():
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, host_inputs, target_s=12.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload's
+    rows (every head of strided rows), scaled to tokens/s by the share of
+    (query, key) pairs the sample covers."""
+    import oracle
+
+    orc = oracle.load()
+    q, k, v, cu = host_inputs
+    T, hq = w.total_tokens, w.n_q_heads
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+    def run(stride):
+        rows = np.arange(stride // 2, T, stride)
+        r = np.repeat(rows, hq)
+        h = np.tile(np.arange(hq), rows.size)
+        t0 = time.perf_counter()
+        orc.attention_rows(q, k, v, cu, w.mask, w.scale, r, h)
+        dt = time.perf_counter() - t0
+        assert w.mask == "causal" and len(w.seq_lens) == 1
+        sample_pairs = int(np.sum(rows + 1)) * hq
+        return dt, sample_pairs, rows.size
+
+    dt, sp, nrows = run(1024)
+    stride = max(1, int(1024 * dt / target_s))
+    if stride < 1024:
+        dt, sp, nrows = run(stride)
+    full_pairs = pairs_of(w) * hq
+    est_full_s = dt * full_pairs / sp
+    return {
+        "value": T / est_full_s,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 C oracle (OpenMP, {threads} threads) on {nrows} rows x {hq} heads "
+                   f"(every {stride}th query row), {sp / full_pairs:.4f} of the workload's "
+                   f"query-key pairs in {dt:.2f} s; scaled to the full workload: "
+                   f"{est_full_s:.1f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also print TFLOP/s for N = 2048..10240 (16/2 heads, causal)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(attention shards by head or sequence with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_attention_prefill_amd as lcap
+    from long_context_attention_prefill_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    lcap.load_library()
+
+    w10 = W.WORKLOADS["3"]
+    host10, dev10 = device_inputs(w10)
+    ms10, out10 = time_calls(w10, dev10, host10[3], args.steps, args.warmup)
+    flops10, bytes10 = algorithmic(w10)
+    tflops10 = flops10 / (ms10 * 1e-3) / 1e12
+
+    # the needle planted at 60 % depth must come back in the last row of every head
+    last = out10[w10.total_tokens - 1].float().cpu().numpy()
+    G = w10.n_q_heads // w10.n_kv_heads
+    for h in range(w10.n_q_heads):
+        c = w10.needle_coords[h // G]
+        assert int(np.argmax(last[h])) == c and last[h, c] >= 0.99, f"needle lost in head {h}"
+
+    w2 = W.WORKLOADS["2"]
+    host2, dev2 = device_inputs(w2)
+    ms2, _ = time_calls(w2, dev2, host2[3], max(args.steps, 1), args.warmup)
+    flops2, _ = algorithmic(w2)
+    tflops2 = flops2 / (ms2 * 1e-3) / 1e12
+
+    sweep = None
+    if args.sweep:
+        sweep = {}
+        for n in (2048, 4096, 6144, 8192, 10240):
+            ws = W.Workload(f"sweep {n}", [0, n], 16, 2, 128, W.BF16, "causal", 1.0, seed=n)
+            hs, ds = device_inputs(ws)
+            ms, _ = time_calls(ws, ds, hs[3], args.steps, args.warmup)
+            sweep[str(n)] = round(algorithmic(ws)[0] / (ms * 1e-3) / 1e12, 1)
+        sweep["flat_ratio_10k_over_2k"] = round(sweep["10240"] / sweep["2048"], 3)
+
+    traffic = read_traffic()
+    line = {
+        "metric": "attention prefill tokens/s (causal bf16, 10k tokens)",
+        "value": round(w10.total_tokens / (ms10 * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms10, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal prefill, 1 sequence x 10240 tokens, 16 query / 2 KV "
+                               "heads, head_dim 128, bf16, needle at 6144",
+                   "seq_len": w10.total_tokens, "global_batch": 1},
+        "tflops": round(tflops10, 1),
+        "pct_bf16_peak": round(100 * tflops10 / PEAK_BF16_TFLOPS, 2),
+        "at_2k": {"workload": "causal, 1 x 2048 tokens, 16/16 heads, d 128, bf16",
+                  "tokens_per_s": round(w2.total_tokens / (ms2 * 1e-3), 1),
+                  "ms_per_step": round(ms2, 5), "tflops": round(tflops2, 1),
+                  "pct_bf16_peak": round(100 * tflops2 / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops10, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops10 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "fwd_bf16<128,4>", "algorithmic_flops": flops10,
+                     "algorithmic_bytes": bytes10},
+    }
+    if sweep is not None:
+        line["sweep_tflops_16x2_causal"] = sweep
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w10, host10)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

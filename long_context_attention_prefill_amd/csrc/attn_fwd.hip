@@ -123,7 +123,7 @@ __device__ __forceinline__ int vt_pos(int kg) {
 }
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16(const LaunchArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(const LaunchArgs a) {
   constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;            // query rows per workgroup
   constexpr int BN = 64;                 // keys per tile
