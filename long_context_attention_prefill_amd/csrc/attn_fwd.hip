@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_launch.h"
 
 namespace attn {
@@ -123,7 +125,7 @@ __device__ __forceinline__ int vt_pos(int kg) {
 }
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(const LaunchArgs a) {
+__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_generic(const LaunchArgs a) {
   constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;            // query rows per workgroup
   constexpr int BN = 64;                 // keys per tile
@@ -422,6 +424,299 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16(const LaunchArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16 / MFMA family, head_dim 64 and 128: K and V reach LDS by direct
+// buffer->LDS loads (no staging registers, rows past the key range read as
+// zeros), rows XOR-swizzled in 16-byte chunks so both the row reads of K and
+// the transposing reads of V are free of bank conflicts, and the V^T operand
+// of O^T = V^T P^T comes from ds_read_b64_tr_b16 on row-major V.
+// ---------------------------------------------------------------------------
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// Chunk swizzle of LDS row r (16-byte chunks; period 16 rows).  Any 16
+// consecutive rows read at one chunk index land in 16 distinct chunk slots
+// of 64 banks (and 8 consecutive rows in distinct slots of 32 banks).
+template <int D>
+__host__ __device__ __forceinline__ constexpr int swz(int r) {
+  if constexpr (D == 128)
+    return r & 15;
+  else
+    return (r & 7) ^ ((r >> 3) & 1);
+}
+
+// Raw buffer descriptor word 3 for gfx9-family parts (32-bit data format).
+constexpr int kBufferWord3 = 0x00020000;
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) {
+  // The host pass only needs this kernel's signature for its launch stub;
+  // the body (gfx950-only builtins) is compiled for the device alone.
+#if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(D == 64 || D == 128, "fast path covers head_dim 64 and 128");
+  constexpr int NT = NW * 64;
+  constexpr int BM = NW * 32;
+  constexpr int BN = 64;
+  constexpr int CH = D / 8;           // 16-byte chunks per row
+  constexpr int KST = D / 16;         // MFMA k steps of S^T
+  constexpr int DB = D / 32;          // 32-row blocks of O^T
+  constexpr int TILE = BN * D;        // bf16 per K (or V) tile buffer
+  constexpr int CHUNKS = BN * CH;     // 16-byte chunks per tile
+  constexpr int LOADS = CHUNKS / NT;  // direct loads per thread, per tile, per tensor
+  static_assert(CHUNKS % NT == 0 && LOADS >= 1, "tile must split evenly over the threads");
+
+  __shared__ __attribute__((aligned(1024))) __bf16 k_lds[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 v_lds[2 * TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  const Item it = decode_item(a, blockIdx.x);
+  const int s0 = a.seq_start[it.seq];
+  const int n = a.seq_len[it.seq];
+  const int h = it.head;
+  const int hk = h / a.group;
+  const int mask = a.mask_kind;
+  const int W = a.window;
+  const float c = a.c;
+  const bool neg = c < 0.0f;
+  const float cabs = neg ? -c : c;
+
+  const int q0 = it.tile * BM;
+  const int qend = min(q0 + BM, n);
+  int kv_lo, kv_hi, tmp;
+  row_range(mask, W, q0, n, kv_lo, tmp);
+  row_range(mask, W, qend - 1, n, tmp, kv_hi);
+
+  const int wq0 = q0 + wave * 32;
+  const bool wave_active = wq0 < n;
+  int w_lo = 0, w_hi = 0, i_lo = 0, i_hi = 0;
+  if (wave_active) {
+    const int wq1 = min(wq0 + 32, n);
+    row_range(mask, W, wq0, n, w_lo, i_hi);
+    row_range(mask, W, wq1 - 1, n, i_lo, w_hi);
+  }
+  const int row = wq0 + l32;
+  const bool row_ok = row < n;
+  int lo_r = 0, hi_r = 0;
+  if (row_ok) row_range(mask, W, row, n, lo_r, hi_r);
+
+  // Q fragments (B operand of S^T = K Q^T): lane (l32, g) holds
+  // q[row][16*kk + 8*g .. +7].
+  bf16x8 qf[KST];
+  {
+    const __bf16 *qrow = reinterpret_cast<const __bf16 *>(a.q) +
+                         ((size_t)(s0 + (row_ok ? row : 0)) * a.hq + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk)
+      qf[kk] = row_ok ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * kk + 8 * g)
+                      : (bf16x8)((__bf16)0.0f);
+  }
+
+  // Direct loads: load i of this wave fills chunk positions
+  // p = (wave*LOADS + i)*64 + lane of the tile, i.e. LDS row p / CH, chunk
+  // slot p % CH, which holds global chunk (p % CH) ^ swz(row).
+  const int rowbytes = a.hkv * D * 2;  // bytes between consecutive tokens of one head
+  uint32_t ld_off[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int p = (wave * LOADS + i) * 64 + lane;
+    const int r = p / CH, cp = p % CH;
+    ld_off[i] = (uint32_t)(r * rowbytes + ((cp ^ swz<D>(r)) * 16));
+  }
+  const char *kseq = reinterpret_cast<const char *>(a.k) + ((size_t)s0 * a.hkv + hk) * D * 2;
+  const char *vseq = reinterpret_cast<const char *>(a.v) + ((size_t)s0 * a.hkv + hk) * D * 2;
+
+  auto issue_loads = [&](int kt, int buf) {
+    const int nrows = min(kv_hi - kt, BN);
+    const int rec = (nrows - 1) * rowbytes + D * 2;  // later rows read as zeros
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(kseq + (size_t)kt * rowbytes), (short)0, rec, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(vseq + (size_t)kt * rowbytes), (short)0, rec, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int slot = (wave * LOADS + i) * 512;  // bf16 elements: 1 KB per wave load
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (lds_void_t *)(k_lds + buf * TILE + slot), 16, ld_off[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (lds_void_t *)(v_lds + buf * TILE + slot), 16, ld_off[i], 0, 0, 0);
+    }
+  };
+
+  // LDS read offsets (elements), constant per lane.  K: row l32 (+32 nb),
+  // chunk 2kk+g.  V (transposing reads): in each 16-lane group, lane 4r+q
+  // points at row 4g + r (+8 for the second half of the k step, +16 ks) and
+  // columns 32db + 16*(lane>>4 & 1) + 4q .. +3.
+  int koff[KST];
+#pragma unroll
+  for (int kk = 0; kk < KST; ++kk) koff[kk] = l32 * D + (((2 * kk + g) ^ swz<D>(l32)) * 8);
+  int voff[DB][2];
+  {
+    const int r = (lane & 15) >> 2;
+    const int half16 = (lane >> 4) & 1;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int vr = 4 * g + r + 8 * hh;
+        const int ck = 4 * db + 2 * half16 + ((lane & 3) >> 1);
+        voff[db][hh] = vr * D + ((ck ^ swz<D>(vr)) * 8) + (lane & 1) * 4;
+      }
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16)(0.0f);
+  float m_run = row_ok ? kNegInf : 0.0f;  // reference maximum, exp2 units
+  float l_run = 0.0f;                     // this lane's share of the row sum
+
+  auto compute = [&](auto masked_tag, auto buf_tag, int kt) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr int BUF = decltype(buf_tag)::value;
+    const __bf16 *kb = k_lds + BUF * TILE;
+    const __bf16 *vb = v_lds + BUF * TILE;
+    f32x16 s[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      s[nb] = (f32x16)(0.0f);
+#pragma unroll
+      for (int kk = 0; kk < KST; ++kk) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + nb * 32 * D + koff[kk]);
+        s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[nb], 0, 0, 0);
+      }
+    }
+    // row maximum of this tile, sign folded in (max of c*s), exp2 units
+    float mx = kNegInf;
+    bool any = true;
+    if constexpr (!MASKED) {
+      if (neg) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, -s[nb][j]);
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[nb][j]);
+      }
+    } else {
+      any = row_ok && kt < hi_r && kt + BN > lo_r;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = kt + nb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+          const bool vis = key >= lo_r && key < hi_r;
+          const float sv = neg ? -s[nb][j] : s[nb][j];
+          mx = vis ? fmaxf(mx, sv) : mx;
+        }
+    }
+    float mt = any ? mx * cabs : kNegInf;
+    mt = fmaxf(mt, xor32(mt));
+    const bool raise = mt > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float m_new = raise ? mt : m_run;
+      const float alpha = raise ? fast_exp2(m_run - m_new) : 1.0f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = -m_run;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float p = fast_exp2(__builtin_fmaf(s[nb][j], c, neg_m));
+        if constexpr (MASKED) {
+          const int key = kt + nb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+          p = (key >= lo_r && key < hi_r) ? p : 0.0f;
+        }
+        s[nb][j] = p;
+      }
+    // P^T fragments: k step ks covers keys 16ks .. 16ks+15 of the tile, held
+    // in accumulator entries 8*(ks&1) .. +7 of block ks>>1.  The row sum is
+    // taken from the same bf16 values the PV product uses.
+    bf16x8 pf[BN / 16];
+    float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int ks = 0; ks < BN / 16; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)s[ks >> 1][8 * (ks & 1) + e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {pf[ks][2 * e], pf[ks][2 * e + 1]};
+        lp[e] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lp[e], false);
+      }
+    }
+    l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ks = 0; ks < BN / 16; ++ks) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t *)(vb + ks * 16 * D + voff[db][0]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t *)(vb + ks * 16 * D + voff[db][1]));
+        const bf16x8 vf = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
+      }
+  };
+
+  auto step = [&](auto buf_tag, int t, int ntiles) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const int kt = kv_lo + t * BN;
+    if (t + 1 < ntiles) issue_loads(kt + BN, BUF ^ 1);
+    if (wave_active && kt < w_hi && kt + BN > w_lo) {
+      if (kt >= i_lo && kt + BN <= i_hi)
+        compute(std::false_type{}, buf_tag, kt);
+      else
+        compute(std::true_type{}, buf_tag, kt);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+
+  const int ntiles = (kv_hi - kv_lo + BN - 1) / BN;
+  issue_loads(kv_lo, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    step(std::integral_constant<int, 0>{}, t, ntiles);
+    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1, ntiles);
+  }
+
+  if (wave_active) {
+    const float l_tot = l_run + xor32(l_run);
+    if (row_ok) {
+      const float inv = 1.0f / l_tot;
+      __bf16 *orow = reinterpret_cast<__bf16 *>(a.out) + ((size_t)(s0 + row) * a.hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d = 32 * db + 8 * jj + 4 * g;
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * jj + e] * inv);
+          *reinterpret_cast<bf16x4 *>(orow + d) = w;
+        }
+    }
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
 // ---------------------------------------------------------------------------
 // fp32 / vector-ALU family
 // ---------------------------------------------------------------------------
@@ -573,9 +868,9 @@ int rows_per_workgroup_f32(int) { return 128; }
 
 int launch_bf16(const LaunchArgs &a, int head_dim, void *stream) {
   switch (head_dim) {
-    case 64: return launch(fwd_bf16<64, kWavesBf16>, a, kWavesBf16 * 64, stream);
-    case 72: return launch(fwd_bf16<72, kWavesBf16>, a, kWavesBf16 * 64, stream);
-    case 128: return launch(fwd_bf16<128, kWavesBf16>, a, kWavesBf16 * 64, stream);
+    case 64: return launch(fwd_bf16_fast<64, kWavesBf16>, a, kWavesBf16 * 64, stream);
+    case 72: return launch(fwd_bf16_generic<72, kWavesBf16>, a, kWavesBf16 * 64, stream);
+    case 128: return launch(fwd_bf16_fast<128, kWavesBf16>, a, kWavesBf16 * 64, stream);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
 }
