@@ -426,11 +426,20 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_generic(const LaunchArgs 
 
 
 // ---------------------------------------------------------------------------
-// bf16 / MFMA family, head_dim 64 and 128: K and V reach LDS by direct
-// buffer->LDS loads (no staging registers, rows past the key range read as
-// zeros), rows XOR-swizzled in 16-byte chunks so both the row reads of K and
-// the transposing reads of V are free of bank conflicts, and the V^T operand
-// of O^T = V^T P^T comes from ds_read_b64_tr_b16 on row-major V.
+// bf16 / MFMA family, head_dim 64 and 128.  K and V reach LDS by direct
+// buffer->LDS loads: no staging registers, and rows past the key range read
+// as zeros (buffer range check).  Both tiles use rows of CH+1 16-byte slots
+// (one slot of padding, filled with zeros by the same loads), and inside
+// each 16-key MFMA step the keys are taken in the order
+//     pi(x) = ((x >> 2) & 1) + 4 (x & 3) + 2 (x >> 3),   x = MFMA row mod 16,
+// so that on gfx950's 64 banks x 4 bytes (b128 reads serve 16 lanes per
+// cycle, b64 reads 32):
+//   - the 16 K rows read together (rows pi(0..15)) start in 16 distinct
+//     16-byte slots mod 256 bytes (odd row stride in slots), and
+//   - the 4 V rows of each transposing read (ds_read_b64_tr_b16) are 4 rows,
+//     i.e. 64 bytes mod 256, apart,
+// both conflict-free, with every LDS address a per-lane base plus an
+// immediate offset.
 // ---------------------------------------------------------------------------
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -438,19 +447,23 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-// Chunk swizzle of LDS row r (16-byte chunks; period 16 rows).  Any 16
-// consecutive rows read at one chunk index land in 16 distinct chunk slots
-// of 64 banks (and 8 consecutive rows in distinct slots of 32 banks).
-template <int D>
-__host__ __device__ __forceinline__ constexpr int swz(int r) {
-  if constexpr (D == 128)
-    return r & 15;
-  else
-    return (r & 7) ^ ((r >> 3) & 1);
-}
-
 // Raw buffer descriptor word 3 for gfx9-family parts (32-bit data format).
 constexpr int kBufferWord3 = 0x00020000;
+// A buffer offset past any key range: the load returns zeros.
+constexpr uint32_t kOutOfRange = 0x7ffffff0u;
+
+template <int D>
+struct FastLayout {
+  static constexpr int CH = D / 8;        // 16-byte chunks of a row in memory
+  static constexpr int SLOTS = CH + 1;    // 16-byte slots per K or V row in LDS
+  static constexpr int ROWB = SLOTS * 16;
+};
+
+// Key (0..31 within a 32-key block) held by MFMA row m of S^T.
+__device__ __forceinline__ int key_of_row(int m) {
+  const int x = m & 15;
+  return 16 * (m >> 4) + ((x >> 2) & 1) + 4 * (x & 3) + 2 * (x >> 3);
+}
 
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) {
@@ -458,19 +471,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
   // the body (gfx950-only builtins) is compiled for the device alone.
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert(D == 64 || D == 128, "fast path covers head_dim 64 and 128");
-  constexpr int NT = NW * 64;
+  using L = FastLayout<D>;
   constexpr int BM = NW * 32;
   constexpr int BN = 64;
-  constexpr int CH = D / 8;           // 16-byte chunks per row
-  constexpr int KST = D / 16;         // MFMA k steps of S^T
-  constexpr int DB = D / 32;          // 32-row blocks of O^T
-  constexpr int TILE = BN * D;        // bf16 per K (or V) tile buffer
-  constexpr int CHUNKS = BN * CH;     // 16-byte chunks per tile
-  constexpr int LOADS = CHUNKS / NT;  // direct loads per thread, per tile, per tensor
-  static_assert(CHUNKS % NT == 0 && LOADS >= 1, "tile must split evenly over the threads");
+  constexpr int CH = L::CH;
+  constexpr int KST = D / 16;  // MFMA k steps of S^T
+  constexpr int DB = D / 32;   // 32-row blocks of O^T
+  constexpr int KBUF = BN * L::ROWB;  // bytes per K (or V) tile buffer
+  constexpr int VBUF = KBUF;
+  // wave-wide direct loads (64 lanes x 16 bytes) per tile and tensor, per wave
+  constexpr int NL = (L::SLOTS + NW - 1) / NW;
 
-  __shared__ __attribute__((aligned(1024))) __bf16 k_lds[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 v_lds[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char k_lds[2 * KBUF];
+  __shared__ __attribute__((aligned(1024))) char v_lds[2 * VBUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -485,7 +498,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
   const int hk = h / a.group;
   const int mask = a.mask_kind;
   const int W = a.window;
-  const float c = a.c;
+  // scale 0 (uniform weights) runs as the smallest normal positive c: every
+  // exp2(c*s) is then 1 in fp32 for |s| < 2^100, and masking by -inf works
+  const float c = a.c == 0.0f ? 0x1p-126f : a.c;
   const bool neg = c < 0.0f;
   const float cabs = neg ? -c : c;
 
@@ -520,181 +535,231 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
                       : (bf16x8)((__bf16)0.0f);
   }
 
-  // Direct loads: load i of this wave fills chunk positions
-  // p = (wave*LOADS + i)*64 + lane of the tile, i.e. LDS row p / CH, chunk
-  // slot p % CH, which holds global chunk (p % CH) ^ swz(row).
+  // Direct loads: wave-wide load j fills LDS slots 64j .. 64j+63 of a tile;
+  // slot p is row p / SLOTS, chunk p % SLOTS (chunks >= CH are padding).
   const int rowbytes = a.hkv * D * 2;  // bytes between consecutive tokens of one head
-  uint32_t ld_off[LOADS];
+  uint32_t ld_off[NL];
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int p = (wave * LOADS + i) * 64 + lane;
-    const int r = p / CH, cp = p % CH;
-    ld_off[i] = (uint32_t)(r * rowbytes + ((cp ^ swz<D>(r)) * 16));
+  for (int i = 0; i < NL; ++i) {
+    const int p = (wave + NW * i) * 64 + lane;
+    const int r = p / L::SLOTS, cs = p % L::SLOTS;
+    ld_off[i] = cs < CH ? (uint32_t)(r * rowbytes + cs * 16) : kOutOfRange;
   }
   const char *kseq = reinterpret_cast<const char *>(a.k) + ((size_t)s0 * a.hkv + hk) * D * 2;
   const char *vseq = reinterpret_cast<const char *>(a.v) + ((size_t)s0 * a.hkv + hk) * D * 2;
 
-  auto issue_loads = [&](int kt, int buf) {
+  // Direct loads of the K (or V) rows kt .. kt+63 into LDS buffer buf.
+  auto issue = [&](const char *seq, char *lds, int kt, int buf) {
     const int nrows = min(kv_hi - kt, BN);
     const int rec = (nrows - 1) * rowbytes + D * 2;  // later rows read as zeros
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(kseq + (size_t)kt * rowbytes), (short)0, rec, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(vseq + (size_t)kt * rowbytes), (short)0, rec, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(seq + (size_t)kt * rowbytes), (short)0, rec, kBufferWord3);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int slot = (wave * LOADS + i) * 512;  // bf16 elements: 1 KB per wave load
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (lds_void_t *)(k_lds + buf * TILE + slot), 16, ld_off[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (lds_void_t *)(v_lds + buf * TILE + slot), 16, ld_off[i], 0, 0, 0);
-    }
+    for (int i = 0; i < NL; ++i)
+      if (wave + NW * i < L::SLOTS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void_t *)(lds + buf * KBUF + (wave + NW * i) * 1024), 16, ld_off[i], 0, 0, 0);
   };
+  auto issue_k = [&](int kt, int buf) { issue(kseq, k_lds, kt, buf); };
+  auto issue_v = [&](int kt, int buf) { issue(vseq, v_lds, kt, buf); };
 
-  // LDS read offsets (elements), constant per lane.  K: row l32 (+32 nb),
-  // chunk 2kk+g.  V (transposing reads): in each 16-lane group, lane 4r+q
-  // points at row 4g + r (+8 for the second half of the k step, +16 ks) and
-  // columns 32db + 16*(lane>>4 & 1) + 4q .. +3.
-  int koff[KST];
-#pragma unroll
-  for (int kk = 0; kk < KST; ++kk) koff[kk] = l32 * D + (((2 * kk + g) ^ swz<D>(l32)) * 8);
-  int voff[DB][2];
-  {
-    const int r = (lane & 15) >> 2;
-    const int half16 = (lane >> 4) & 1;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int vr = 4 * g + r + 8 * hh;
-        const int ck = 4 * db + 2 * half16 + ((lane & 3) >> 1);
-        voff[db][hh] = vr * D + ((ck ^ swz<D>(vr)) * 8) + (lane & 1) * 4;
-      }
-  }
+  // Per-lane LDS read bases (bytes); every other term is an immediate.
+  //   K: MFMA row l32 of S^T is key key_of_row(l32) (+32 nb); chunk 2kk + g.
+  //   V: in each 16-lane group, lane 4r+q points at key g + 4r (+2 for the
+  //   second half of a k step, +16 per k step) and columns
+  //   32db + 16*(lane>>4 & 1) + 4q .. +3; the transpose hands lane j of the
+  //   group column j of those four keys, in the order P holds them.
+  const int kread = key_of_row(l32) * L::ROWB + 16 * g;
+  const int vread = (g + 4 * ((lane & 15) >> 2)) * L::ROWB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = (f32x16)(0.0f);
-  float m_run = row_ok ? kNegInf : 0.0f;  // reference maximum, exp2 units
-  float l_run = 0.0f;                     // this lane's share of the row sum
+  float l_run = 0.0f;  // this lane's share of the row sum
+  // Softmax reference of the row in exp2 units, fixed for a whole sweep: the
+  // maximum of the first tile holding keys visible to the row.  Later keys
+  // may score higher, so probabilities exp2(c*s - m) may exceed 1 (fp32 and
+  // bf16 keep the same 8 exponent bits, so relative precision is unchanged)
+  // and O is never rescaled.  If a row's sum or output comes out non-finite
+  // (a score more than ~127 doublings above that first maximum), the
+  // workgroup sweeps once more for the exact row maximum and then repeats
+  // the accumulation with it, where no probability exceeds 1.
+  float m_ref = row_ok ? kNegInf : 0.0f;
 
-  auto compute = [&](auto masked_tag, auto buf_tag, int kt) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    constexpr int BUF = decltype(buf_tag)::value;
-    const __bf16 *kb = k_lds + BUF * TILE;
-    const __bf16 *vb = v_lds + BUF * TILE;
-    f32x16 s[2];
+  // accumulator entry j of block nb (lane half g) holds key
+  // kt + 32 nb + key_of_row(8 (j >> 2) + 4 g + (j & 3))
+  auto visible = [&](int kt, int nb, int j) {
+    const int key = kt + nb * 32 + 16 * (j >> 3) + 2 * ((j >> 2) & 1) + 4 * (j & 3) + g;
+    return key >= lo_r && key < hi_r;
+  };
+  // a score that becomes -inf once multiplied by c
+  const float s_void = neg ? __builtin_huge_valf() : kNegInf;
+
+  // S^T = K Q^T for the 64 keys held in K buffer KB.
+  auto qk = [&](auto kbuf_tag, f32x16 (&sc)[2]) {
+    constexpr int KB = decltype(kbuf_tag)::value;
+    const char *kb = k_lds + KB * KBUF + kread;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      s[nb] = (f32x16)(0.0f);
+      sc[nb] = (f32x16)(0.0f);
 #pragma unroll
       for (int kk = 0; kk < KST; ++kk) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + nb * 32 * D + koff[kk]);
-        s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[nb], 0, 0, 0);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + nb * 32 * L::ROWB + kk * 32);
+        sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc[nb], 0, 0, 0);
       }
     }
-    // row maximum of this tile, sign folded in (max of c*s), exp2 units
-    float mx = kNegInf;
-    bool any = true;
-    if constexpr (!MASKED) {
-      if (neg) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, -s[nb][j]);
-      } else {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[nb][j]);
-      }
-    } else {
-      any = row_ok && kt < hi_r && kt + BN > lo_r;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = kt + nb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-          const bool vis = key >= lo_r && key < hi_r;
-          const float sv = neg ? -s[nb][j] : s[nb][j];
-          mx = vis ? fmaxf(mx, sv) : mx;
-        }
-    }
-    float mt = any ? mx * cabs : kNegInf;
-    mt = fmaxf(mt, xor32(mt));
-    const bool raise = mt > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(raise)) {
-      const float m_new = raise ? mt : m_run;
-      const float alpha = raise ? fast_exp2(m_run - m_new) : 1.0f;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = -m_run;
+  };
+  auto apply_mask = [&](f32x16 (&sc)[2], int kt) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float p = fast_exp2(__builtin_fmaf(s[nb][j], c, neg_m));
-        if constexpr (MASKED) {
-          const int key = kt + nb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-          p = (key >= lo_r && key < hi_r) ? p : 0.0f;
-        }
-        s[nb][j] = p;
-      }
-    // P^T fragments: k step ks covers keys 16ks .. 16ks+15 of the tile, held
-    // in accumulator entries 8*(ks&1) .. +7 of block ks>>1.  The row sum is
-    // taken from the same bf16 values the PV product uses.
-    bf16x8 pf[BN / 16];
-    float lp[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j = 0; j < 16; ++j) sc[nb][j] = visible(kt, nb, j) ? sc[nb][j] : s_void;
+  };
+  // Row maximum of c*s over the tile, both lane halves combined.
+  auto row_max = [&](const f32x16 (&sc)[2]) {
+    float mx = kNegInf;
+    if (neg) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, -sc[nb][j]);
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[nb][j]);
+    }
+    const float mt = mx * cabs;
+    return fmaxf(mt, xor32(mt));
+  };
+  // P = exp2(c*s - m) as bf16 B operands of O^T = V^T P^T, and the row sum
+  // of those same bf16 values.  k step ks covers keys 16ks .. 16ks+15, held
+  // in accumulator entries 8*(ks&1) .. +7 of block ks>>1; entry e of lane
+  // half g is key 16ks + g + 4(e & 3) + 2(e >> 2).
+  auto softmax = [&](f32x16 (&sc)[2], bf16x8 (&pf)[BN / 16]) {
+    // a row with no visible key yet has every score at -inf here
+    const float neg_m = m_ref == kNegInf ? 0.0f : -m_ref;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int ks = 0; ks < BN / 16; ++ks) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)s[ks >> 1][8 * (ks & 1) + e];
+      for (int e = 0; e < 8; ++e)
+        pf[ks][e] = (__bf16)fast_exp2(__builtin_fmaf(sc[ks >> 1][8 * (ks & 1) + e], c, neg_m));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bf16x2 pr = {pf[ks][2 * e], pf[ks][2 * e + 1]};
-        lp[e] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lp[e], false);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
       }
     }
-    l_run += (lp[0] + lp[1]) + (lp[2] + lp[3]);
+  };
+  // O += P V with V from V buffer VB.
+  auto pv = [&](auto vbuf_tag, const bf16x8 (&pf)[BN / 16]) {
+    constexpr int VB = decltype(vbuf_tag)::value;
+    const char *vb = v_lds + VB * VBUF + vread;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int ks = 0; ks < BN / 16; ++ks) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t *)(vb + ks * 16 * D + voff[db][0]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t *)(vb + ks * 16 * D + voff[db][1]));
+        const char *vp = vb + ks * 16 * L::ROWB + db * 64;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp + 2 * L::ROWB));
         const bf16x8 vf = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
       }
   };
 
-  auto step = [&](auto buf_tag, int t, int ntiles) {
-    constexpr int BUF = decltype(buf_tag)::value;
+  const int ntiles = (kv_hi - kv_lo + BN - 1) / BN;
+  auto wave_sees = [&](int t) {
     const int kt = kv_lo + t * BN;
-    if (t + 1 < ntiles) issue_loads(kt + BN, BUF ^ 1);
-    if (wave_active && kt < w_hi && kt + BN > w_lo) {
-      if (kt >= i_lo && kt + BN <= i_hi)
-        compute(std::false_type{}, buf_tag, kt);
-      else
-        compute(std::true_type{}, buf_tag, kt);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    return t < ntiles && kt < w_hi && kt + BN > w_lo;
+  };
+  auto needs_mask = [&](int t) {
+    const int kt = kv_lo + t * BN;
+    return kt < i_lo || kt + BN > i_hi;
   };
 
-  const int ntiles = (kv_hi - kv_lo + BN - 1) / BN;
-  issue_loads(kv_lo, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
-    step(std::integral_constant<int, 0>{}, t, ntiles);
-    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1, ntiles);
+  // Accumulating sweep over the double-buffered K/V tiles: the loads of
+  // tile t+1 are in flight while tile t is computed.
+  bool redo = wave_active;  // this wave computes in the current sweep
+  auto accumulate_sweep = [&]() {
+    auto step = [&](auto buf_tag, int t) {
+      constexpr int BUF = decltype(buf_tag)::value;
+      const int kt = kv_lo + t * BN;
+      if (t + 1 < ntiles) {
+        issue_k(kt + BN, BUF ^ 1);
+        issue_v(kt + BN, BUF ^ 1);
+      }
+      if (redo && wave_sees(t)) {
+        f32x16 sc[2];
+        qk(buf_tag, sc);
+        if (needs_mask(t)) apply_mask(sc, kt);
+        if (__builtin_amdgcn_ballot_w64(m_ref == kNegInf)) {
+          const float mt = row_max(sc);
+          m_ref = m_ref == kNegInf ? mt : m_ref;
+        }
+        bf16x8 pf[BN / 16];
+        softmax(sc, pf);
+        pv(buf_tag, pf);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    issue_k(kv_lo, 0);
+    issue_v(kv_lo, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
+    }
+  };
+  // Exact row maxima (after an overflow): scores only, no accumulation.
+  auto max_sweep = [&]() {
+    auto step = [&](auto buf_tag, int t) {
+      constexpr int BUF = decltype(buf_tag)::value;
+      const int kt = kv_lo + t * BN;
+      if (t + 1 < ntiles) issue_k(kt + BN, BUF ^ 1);
+      if (redo && wave_sees(t)) {
+        f32x16 sc[2];
+        qk(buf_tag, sc);
+        if (needs_mask(t)) apply_mask(sc, kt);
+        m_ref = fmaxf(m_ref, row_max(sc));
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    issue_k(kv_lo, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
+    }
+  };
+
+  for (int pass = 0;; ++pass) {
+    accumulate_sweep();
+    if (pass == 1) break;
+    // Rows whose first pass overflowed are redone with exact maxima.
+    bool bad = false;
+    if (wave_active) {
+      const float l_tot = l_run + xor32(l_run);
+      bad = row_ok && !__builtin_isfinite(l_tot);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) bad = bad || (row_ok && !__builtin_isfinite(o[db][j]));
+    }
+    redo = __builtin_amdgcn_ballot_w64(bad) != 0;
+    if (!__syncthreads_or(redo)) break;
+    if (redo) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = (f32x16)(0.0f);
+      l_run = 0.0f;
+      m_ref = row_ok ? kNegInf : 0.0f;
+    }
+    max_sweep();
   }
 
   if (wave_active) {
