@@ -482,8 +482,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
   // wave-wide direct loads (64 lanes x 16 bytes) per tile and tensor, per wave
   constexpr int NL = (L::SLOTS + NW - 1) / NW;
 
-  __shared__ __attribute__((aligned(1024))) char k_lds[2 * KBUF];
-  __shared__ __attribute__((aligned(1024))) char v_lds[2 * VBUF];
+  // One array per buffer half: the compiler can then tell that a direct
+  // load into one half does not feed reads of the other, and does not make
+  // those reads wait for the load.
+  __shared__ __attribute__((aligned(1024))) char k_lds0[KBUF];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[KBUF];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[VBUF];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[VBUF];
+  auto k_buf = [](auto tag) -> char * {
+    if constexpr (decltype(tag)::value == 0) return k_lds0; else return k_lds1;
+  };
+  auto v_buf = [](auto tag) -> char * {
+    if constexpr (decltype(tag)::value == 0) return v_lds0; else return v_lds1;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -548,8 +559,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
   const char *kseq = reinterpret_cast<const char *>(a.k) + ((size_t)s0 * a.hkv + hk) * D * 2;
   const char *vseq = reinterpret_cast<const char *>(a.v) + ((size_t)s0 * a.hkv + hk) * D * 2;
 
-  // Direct loads of the K (or V) rows kt .. kt+63 into LDS buffer buf.
-  auto issue = [&](const char *seq, char *lds, int kt, int buf) {
+  // Direct loads of the K (or V) rows kt .. kt+63 into an LDS buffer.
+  auto issue = [&](const char *seq, char *lds, int kt) {
     const int nrows = min(kv_hi - kt, BN);
     const int rec = (nrows - 1) * rowbytes + D * 2;  // later rows read as zeros
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -558,10 +569,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
     for (int i = 0; i < NL; ++i)
       if (wave + NW * i < L::SLOTS)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_void_t *)(lds + buf * KBUF + (wave + NW * i) * 1024), 16, ld_off[i], 0, 0, 0);
+            rs, (lds_void_t *)(lds + (wave + NW * i) * 1024), 16, ld_off[i], 0, 0, 0);
   };
-  auto issue_k = [&](int kt, int buf) { issue(kseq, k_lds, kt, buf); };
-  auto issue_v = [&](int kt, int buf) { issue(vseq, v_lds, kt, buf); };
+  auto issue_k = [&](int kt, auto buf_tag) { issue(kseq, k_buf(buf_tag), kt); };
+  auto issue_v = [&](int kt, auto buf_tag) { issue(vseq, v_buf(buf_tag), kt); };
 
   // Per-lane LDS read bases (bytes); every other term is an immediate.
   //   K: MFMA row l32 of S^T is key key_of_row(l32) (+32 nb); chunk 2kk + g.
@@ -598,7 +609,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
   // S^T = K Q^T for the 64 keys held in K buffer KB.
   auto qk = [&](auto kbuf_tag, f32x16 (&sc)[2]) {
     constexpr int KB = decltype(kbuf_tag)::value;
-    const char *kb = k_lds + KB * KBUF + kread;
+    const char *kb = k_buf(kbuf_tag) + kread;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       sc[nb] = (f32x16)(0.0f);
@@ -655,7 +666,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
   // O += P V with V from V buffer VB.
   auto pv = [&](auto vbuf_tag, const bf16x8 (&pf)[BN / 16]) {
     constexpr int VB = decltype(vbuf_tag)::value;
-    const char *vb = v_lds + VB * VBUF + vread;
+    const char *vb = v_buf(vbuf_tag) + vread;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -687,8 +698,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
       constexpr int BUF = decltype(buf_tag)::value;
       const int kt = kv_lo + t * BN;
       if (t + 1 < ntiles) {
-        issue_k(kt + BN, BUF ^ 1);
-        issue_v(kt + BN, BUF ^ 1);
+        issue_k(kt + BN, std::integral_constant<int, BUF ^ 1>{});
+        issue_v(kt + BN, std::integral_constant<int, BUF ^ 1>{});
       }
       if (redo && wave_sees(t)) {
         f32x16 sc[2];
@@ -705,8 +716,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     };
-    issue_k(kv_lo, 0);
-    issue_v(kv_lo, 0);
+    issue_k(kv_lo, std::integral_constant<int, 0>{});
+    issue_v(kv_lo, std::integral_constant<int, 0>{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < ntiles; t += 2) {
@@ -719,7 +730,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
     auto step = [&](auto buf_tag, int t) {
       constexpr int BUF = decltype(buf_tag)::value;
       const int kt = kv_lo + t * BN;
-      if (t + 1 < ntiles) issue_k(kt + BN, BUF ^ 1);
+      if (t + 1 < ntiles) issue_k(kt + BN, std::integral_constant<int, BUF ^ 1>{});
       if (redo && wave_sees(t)) {
         f32x16 sc[2];
         qk(buf_tag, sc);
@@ -729,7 +740,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     };
-    issue_k(kv_lo, 0);
+    issue_k(kv_lo, std::integral_constant<int, 0>{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < ntiles; t += 2) {
