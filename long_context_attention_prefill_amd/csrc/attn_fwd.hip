@@ -620,6 +620,37 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
       }
     }
   };
+  // Schedule of a plain tile (one basic block): the MFMAs of the second
+  // 32-key block of S^T run under the softmax of the first, and the PV MFMAs
+  // of the first two k steps under the softmax of the second, with a few LDS
+  // reads kept ahead of their MFMAs (mask: 2 VALU, 8 MFMA, 0x100 DS read).
+  auto plain_tile_schedule = [&]() {
+    constexpr int SOFT = 3 * (BN / 2) / KST;  // softmax VALU ops per QK MFMA
+    constexpr int PV_HALF = DB * (BN / 32);   // PV MFMAs per pair of k steps
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < KST; ++i) {  // S^T block 0
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < KST; ++i) {  // S^T block 1 under softmax of block 0
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, SOFT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < PV_HALF; ++i) {  // PV of k steps 0-1 under softmax of block 1
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2 * KST * SOFT / PV_HALF, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < PV_HALF; ++i) {  // PV of k steps 2-3
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
   auto apply_mask = [&](f32x16 (&sc)[2], int kt) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
@@ -668,9 +699,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
     constexpr int VB = decltype(vbuf_tag)::value;
     const char *vb = v_buf(vbuf_tag) + vread;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int ks = 0; ks < BN / 16; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < BN / 16; ++ks) {
+      for (int db = 0; db < DB; ++db) {
         const char *vp = vb + ks * 16 * L::ROWB + db * 64;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp + 2 * L::ROWB));
@@ -683,55 +714,130 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
   const int ntiles = (kv_hi - kv_lo + BN - 1) / BN;
   auto wave_sees = [&](int t) {
     const int kt = kv_lo + t * BN;
-    return t < ntiles && kt < w_hi && kt + BN > w_lo;
+    return kt < w_hi && kt + BN > w_lo;
   };
   auto needs_mask = [&](int t) {
     const int kt = kv_lo + t * BN;
     return kt < i_lo || kt + BN > i_hi;
   };
+  // Key tiles inside every row's visible range of the workgroup (the
+  // intersection [lo(last row), hi(first row)) of its rows) need no mask for
+  // any wave: they form one run [t_plain0, t_plain1) of the sweep.  The first
+  // tile always takes the general step, which sets the softmax reference.
+  int t_plain0 = 1, t_plain1 = 1;
+  {
+    int wlo, whi, tmp2;
+    row_range(mask, W, qend - 1, n, wlo, tmp2);
+    row_range(mask, W, q0, n, tmp2, whi);
+    const int first = max(1, (wlo - kv_lo + BN - 1) / BN);
+    const int last = max(0, (whi - kv_lo) / BN);  // tiles [0, last) end at or before whi
+    if (last > first) {
+      t_plain0 = first;
+      t_plain1 = last;
+    }
+  }
+  auto k_rt = [&](int buf) -> const char * { return buf ? k_lds1 : k_lds0; };
+  auto v_rt = [&](int buf) -> const char * { return buf ? v_lds1 : v_lds0; };
 
-  // Accumulating sweep over the double-buffered K/V tiles: the loads of
-  // tile t+1 are in flight while tile t is computed.
-  bool redo = wave_active;  // this wave computes in the current sweep
-  auto accumulate_sweep = [&]() {
-    auto step = [&](auto buf_tag, int t) {
-      constexpr int BUF = decltype(buf_tag)::value;
-      const int kt = kv_lo + t * BN;
-      if (t + 1 < ntiles) {
-        issue_k(kt + BN, std::integral_constant<int, BUF ^ 1>{});
-        issue_v(kt + BN, std::integral_constant<int, BUF ^ 1>{});
+  // General step (first tile, diagonal and edge tiles): scores of a tile the
+  // wave does not see are voided (P = 0); masking and the reference update
+  // touch only S and m_ref, then the same softmax and PV run.
+  auto general_step = [&](int t) __attribute__((always_inline)) {
+    const int kt = kv_lo + t * BN;
+    const int buf = t & 1;
+    if (t + 1 < ntiles) {
+      if (buf) {
+        issue_k(kt + BN, std::integral_constant<int, 0>{});
+        issue_v(kt + BN, std::integral_constant<int, 0>{});
+      } else {
+        issue_k(kt + BN, std::integral_constant<int, 1>{});
+        issue_v(kt + BN, std::integral_constant<int, 1>{});
       }
-      if (redo && wave_sees(t)) {
-        f32x16 sc[2];
-        qk(buf_tag, sc);
-        if (needs_mask(t)) apply_mask(sc, kt);
-        if (__builtin_amdgcn_ballot_w64(m_ref == kNegInf)) {
-          const float mt = row_max(sc);
-          m_ref = m_ref == kNegInf ? mt : m_ref;
+    }
+    f32x16 sc[2];
+    {
+      const char *kb = k_rt(buf) + kread;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        sc[nb] = (f32x16)(0.0f);
+#pragma unroll
+        for (int kk = 0; kk < KST; ++kk) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + nb * 32 * L::ROWB + kk * 32);
+          sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc[nb], 0, 0, 0);
         }
-        bf16x8 pf[BN / 16];
-        softmax(sc, pf);
-        pv(buf_tag, pf);
       }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    };
+    }
+    if (!wave_sees(t)) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) sc[nb] = (f32x16)(s_void);
+    } else if (needs_mask(t)) {
+      apply_mask(sc, kt);
+    }
+    if (__builtin_amdgcn_ballot_w64(m_ref == kNegInf)) {
+      const float mt = row_max(sc);
+      m_ref = m_ref == kNegInf ? mt : m_ref;
+    }
+    bf16x8 pf[BN / 16];
+    softmax(sc, pf);
+    {
+      const char *vb = v_rt(buf) + vread;
+#pragma unroll
+      for (int ks = 0; ks < BN / 16; ++ks)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const char *vp = vb + ks * 16 * L::ROWB + db * 64;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp));
+          const i16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp + 2 * L::ROWB));
+          const bf16x8 vf = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  // Plain step: one basic block, scheduled so MFMA and softmax work overlap.
+  auto plain_step = [&](auto buf_tag, int t) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const int kt = kv_lo + t * BN;
+    if (t + 1 < ntiles) {
+      issue_k(kt + BN, std::integral_constant<int, BUF ^ 1>{});
+      issue_v(kt + BN, std::integral_constant<int, BUF ^ 1>{});
+    }
+    f32x16 sc[2];
+    bf16x8 pf[BN / 16];
+    qk(buf_tag, sc);
+    softmax(sc, pf);
+    pv(buf_tag, pf);
+    plain_tile_schedule();
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  // Accumulating sweep over the double-buffered K/V tiles; the loads of tile
+  // t+1 are in flight while tile t is computed.
+  auto accumulate_sweep = [&]() __attribute__((always_inline)) {
     issue_k(kv_lo, std::integral_constant<int, 0>{});
     issue_v(kv_lo, std::integral_constant<int, 0>{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int t = 0; t < ntiles; t += 2) {
-      step(std::integral_constant<int, 0>{}, t);
-      if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
+    int t = 0;
+    for (; t < t_plain0 && t < ntiles; ++t) general_step(t);
+    if (t < t_plain1 && (t & 1)) plain_step(std::integral_constant<int, 1>{}, t++);
+    for (; t + 1 < t_plain1; t += 2) {
+      plain_step(std::integral_constant<int, 0>{}, t);
+      plain_step(std::integral_constant<int, 1>{}, t + 1);
     }
+    if (t < t_plain1) plain_step(std::integral_constant<int, 0>{}, t++);
+    for (; t < ntiles; ++t) general_step(t);
   };
   // Exact row maxima (after an overflow): scores only, no accumulation.
-  auto max_sweep = [&]() {
+  auto max_sweep = [&]() __attribute__((always_inline)) {
     auto step = [&](auto buf_tag, int t) {
       constexpr int BUF = decltype(buf_tag)::value;
       const int kt = kv_lo + t * BN;
       if (t + 1 < ntiles) issue_k(kt + BN, std::integral_constant<int, BUF ^ 1>{});
-      if (redo && wave_sees(t)) {
+      if (wave_sees(t)) {
         f32x16 sc[2];
         qk(buf_tag, sc);
         if (needs_mask(t)) apply_mask(sc, kt);
@@ -752,7 +858,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
   for (int pass = 0;; ++pass) {
     accumulate_sweep();
     if (pass == 1) break;
-    // Rows whose first pass overflowed are redone with exact maxima.
+    // A row whose sum or output overflowed: the workgroup redoes its rows
+    // with the exact row maxima as references.
     bool bad = false;
     if (wave_active) {
       const float l_tot = l_run + xor32(l_run);
@@ -762,14 +869,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
 #pragma unroll
         for (int j = 0; j < 16; ++j) bad = bad || (row_ok && !__builtin_isfinite(o[db][j]));
     }
-    redo = __builtin_amdgcn_ballot_w64(bad) != 0;
-    if (!__syncthreads_or(redo)) break;
-    if (redo) {
+    if (!__syncthreads_or(bad)) break;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] = (f32x16)(0.0f);
-      l_run = 0.0f;
-      m_ref = row_ok ? kNegInf : 0.0f;
-    }
+    for (int db = 0; db < DB; ++db) o[db] = (f32x16)(0.0f);
+    l_run = 0.0f;
+    m_ref = row_ok ? kNegInf : 0.0f;
     max_sweep();
   }
 
