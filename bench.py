@@ -4,10 +4,15 @@ A step is one ``attn_prefill`` call (the whole fused path: planning, K/V
 streaming, QK^T, mask, online softmax, PV, epilogue) over one batch of seeded
 synthetic input already resident in HBM.  The headline workload is causal
 bf16 prefill of one 10240-token sequence, 16 query / 2 KV heads, head dim
-128, with the needle planted at 60 % depth; the 2048-token causal case
-(16/16 heads) is timed beside it.  Prints ONE JSON line.
+128, with the needle planted at 60 % depth.  Beside it, each at its own
+shape: causal 2048 tokens (16/16 heads), and the packed 4-sequence batch
+(2048 + 5120 + 8192 + 10240 tokens, 16/2 heads) under the causal and the
+256-token window mask.  Each of these is timed as >= 20 samples of R
+back-to-back calls (R chosen so a sample lasts >= 1 ms) between two events,
+reported per call as median / min / p90.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--sweep]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only]
+                    [--no-cpu-baseline] [--sweep] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -89,6 +94,67 @@ def time_calls(w, dev, cu, steps, warmup):
     return start.elapsed_time(end) / steps, out
 
 
+def sample_calls(w, dev, cu, n_samples=20, min_ms=1.0):
+    """Per-call ms of n_samples samples, each R back-to-back calls between two
+    events on the launch stream, R chosen so one sample lasts >= min_ms."""
+    import torch
+
+    import long_context_attention_prefill_amd as lcap
+
+    q, k, v = dev
+    out = torch.empty_like(q)
+    cu_l = [int(x) for x in cu]
+    stream = torch.cuda.current_stream()
+    for _ in range(5):
+        lcap.attn_prefill(q, k, v, cu_l, mask=w.mask, scale=w.scale, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    lcap.attn_prefill(q, k, v, cu_l, mask=w.mask, scale=w.scale, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    reps = max(1, int(math.ceil(min_ms / max(e0.elapsed_time(e1), 1e-3))))
+    per_call = []
+    for _ in range(n_samples):
+        e0.record(stream)
+        for _ in range(reps):
+            lcap.attn_prefill(q, k, v, cu_l, mask=w.mask, scale=w.scale, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_call.append(e0.elapsed_time(e1) / reps)
+    return np.array(per_call), reps
+
+
+def summarize(w, per_call_ms, reps):
+    """tokens/s, TFLOP/s and HBM rate of one workload from per-call times."""
+    flops, byts = algorithmic(w)
+    med = float(np.median(per_call_ms))
+    res = {"workload": w.name, "ms_median": round(med, 5),
+           "ms_min": round(float(per_call_ms.min()), 5),
+           "ms_p90": round(float(np.percentile(per_call_ms, 90)), 5),
+           "samples": int(per_call_ms.size), "calls_per_sample": reps,
+           "tokens_per_s": round(w.total_tokens / (med * 1e-3), 1),
+           "tflops": round(flops / (med * 1e-3) / 1e12, 1),
+           "pct_bf16_peak": round(100 * flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+    hbm = byts / (med * 1e-3) / 1e9
+    res["algorithmic_hbm_gbs"] = round(hbm, 1)
+    res["pct_hbm_peak"] = round(100 * hbm / PEAK_HBM_GBS, 2)
+    return res
+
+
+def gpu_clock():
+    """Current shader clock as rocm-smi reports it (best effort, text)."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        for line in r.stdout.splitlines():
+            if "sclk" in line:
+                return line.strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return None
+
+
 def kernel_digest():
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -157,7 +223,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--skip-2k", action="store_true",
+    ap.add_argument("--headline-only", action="store_true",
                     help="time only the 10k workload (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
@@ -191,13 +257,17 @@ def main():
         c = w10.needle_coords[h // G]
         assert int(np.argmax(last[h])) == c and last[h, c] >= 0.99, f"needle lost in head {h}"
 
-    w2 = W.WORKLOADS["2"]
-    ms2 = tflops2 = float("nan")
-    if not args.skip_2k:
-        host2, dev2 = device_inputs(w2)
-        ms2, _ = time_calls(w2, dev2, host2[3], max(args.steps, 1), args.warmup)
-        flops2, _ = algorithmic(w2)
-        tflops2 = flops2 / (ms2 * 1e-3) / 1e12
+    stats10 = None
+    others = {}
+    if not args.headline_only:
+        stats10 = summarize(w10, *sample_calls(w10, dev10, host10[3]))
+        del dev10[:]
+        for key in ("2", "5a", "5b"):
+            w = W.WORKLOADS[key]
+            hst, dv = device_inputs(w)
+            others[key] = summarize(w, *sample_calls(w, dv, hst[3]))
+            del dv
+        torch.cuda.empty_cache()
 
     sweep = None
     if args.sweep:
@@ -236,16 +306,18 @@ def main():
                    "seq_len": w10.total_tokens, "global_batch": 1},
         "tflops": round(tflops10, 1),
         "pct_bf16_peak": round(100 * tflops10 / PEAK_BF16_TFLOPS, 2),
-        "at_2k": None if args.skip_2k else {"workload": "causal, 1 x 2048 tokens, 16/16 heads, d 128, bf16",
-                  "tokens_per_s": round(w2.total_tokens / (ms2 * 1e-3), 1),
-                  "ms_per_step": round(ms2, 5), "tflops": round(tflops2, 1),
-                  "pct_bf16_peak": round(100 * tflops2 / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(tflops10, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops10 / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": "fwd_bf16_fast<128,4>", "algorithmic_flops": flops10,
+                     "kernel": "fwd_bf16_fast<128,4,1>", "algorithmic_flops": flops10,
                      "algorithmic_bytes": bytes10},
     }
+    if stats10 is not None:
+        line["samples_10k"] = stats10
+        line["at_2k"] = others["2"]
+        line["packed_causal_5a"] = others["5a"]
+        line["packed_window256_5b"] = others["5b"]
+        line["gpu_clock"] = gpu_clock()
     if sweep is not None:
         line["sweep_tflops_16x2_causal"] = sweep
     if not args.no_cpu_baseline:

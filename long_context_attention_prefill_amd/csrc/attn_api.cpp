@@ -122,6 +122,15 @@ int attn_prefill(const void *q, const void *k, const void *v, void *out,
     }
     if (items > INT32_MAX) return ATTN_EUNSUPPORTED;
     a.total_items = static_cast<int32_t>(items);
+    // causal item order: levels [seq_tiles[k], seq_tiles[k-1]) of the k longest
+    // sequences follow each other, longest level first
+    int64_t start = 0;
+    for (size_t k = 1; k <= cnt; ++k) {
+      a.level_start[k - 1] = static_cast<int32_t>(start);
+      const int32_t below = k < cnt ? a.seq_tiles[k] : 0;
+      start += static_cast<int64_t>(a.seq_tiles[k - 1] - below) * static_cast<int64_t>(k) * n_q_heads;
+    }
+    a.level_start[cnt] = static_cast<int32_t>(start);  // == total_items
     plan.push_back(a);
   }
   for (const attn::LaunchArgs &la : plan) {

@@ -59,9 +59,12 @@ struct Item {
 
 // Workgroup r -> (sequence, query tile, query head), heaviest work first.
 // Causal: tile m costs ~(m+1) key tiles in every sequence, so items are
-// ordered by m descending across the batch; otherwise by sequence length
-// (sequences arrive longest first).  The hq heads of one (sequence, tile)
-// are consecutive, and when hq is a multiple of 8 slot s maps to head
+// ordered by m descending across the batch, the sequences holding a level in
+// length order; the levels where the k longest sequences are active form one
+// segment, starting at item level_start[k-1], so the decode scans segments
+// (at most one per sequence), not levels.  Otherwise items go by sequence
+// length (sequences arrive longest first).  The hq heads of one (sequence,
+// tile) are consecutive, and when hq is a multiple of 8 slot s maps to head
 // (s % 8) * (hq / 8) + s / 8: consecutive workgroups land on different XCDs
 // round-robin, so each XCD keeps to a contiguous block of query heads, i.e.
 // to few key/value heads, and their K/V stays in that XCD's L2.
@@ -69,18 +72,15 @@ __device__ Item decode_item(const LaunchArgs &a, int r) {
   Item it{0, 0, 0};
   int slot = 0;
   if (a.mask_kind == kCausal) {
-    int ptr = 0;
-    for (int m = a.seq_tiles[0] - 1; m >= 0; --m) {
-      while (ptr < a.n_seqs && a.seq_tiles[ptr] > m) ++ptr;
-      const int cnt = ptr * a.hq;
-      if (r < cnt) {
-        it.seq = r / a.hq;
-        it.tile = m;
-        slot = r - it.seq * a.hq;
-        break;
-      }
-      r -= cnt;
-    }
+    int k = 1;  // segment: the k longest sequences are active
+    while (k < a.n_seqs && a.level_start[k] <= r) ++k;
+    const int rel = r - a.level_start[k - 1];
+    const int per_level = k * a.hq;
+    const int lvl = rel / per_level;
+    const int rem = rel - lvl * per_level;
+    it.tile = a.seq_tiles[k - 1] - 1 - lvl;
+    it.seq = rem / a.hq;
+    slot = rem - it.seq * a.hq;
   } else {
     for (int b = 0; b < a.n_seqs; ++b) {
       const int cnt = a.seq_tiles[b] * a.hq;
@@ -465,30 +465,44 @@ __device__ __forceinline__ int key_of_row(int m) {
   return 16 * (m >> 4) + ((x >> 2) & 1) + 4 * (x & 3) + 2 * (x >> 3);
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) {
+// Each wave owns R consecutive 32-row query sub-blocks (the workgroup covers
+// NW * 32 * R rows); every K or V fragment read from LDS feeds the R
+// sub-blocks' MFMAs back to back.  R = 1 runs two workgroups per CU (two waves
+// per SIMD, up to 256 registers each) and is the instance dispatched.  R = 2
+// (one wave per SIMD, up to 512 registers) halves the LDS reads and K/V tile
+// loads per MFMA, but with no second wave to hide latency and its scores
+// spilling into AGPRs it measured ~30 % slower on gfx950, so it is not
+// instantiated.
+template <int D, int NW, int R>
+__global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs a) {
   // The host pass only needs this kernel's signature for its launch stub;
   // the body (gfx950-only builtins) is compiled for the device alone.
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert(D == 64 || D == 128, "fast path covers head_dim 64 and 128");
+  static_assert(R == 1 || R == 2, "one or two query sub-blocks per wave");
   using L = FastLayout<D>;
-  constexpr int BM = NW * 32;
+  constexpr int BM = NW * 32 * R;
   constexpr int BN = 64;
   constexpr int CH = L::CH;
   constexpr int KST = D / 16;  // MFMA k steps of S^T
   constexpr int DB = D / 32;   // 32-row blocks of O^T
-  constexpr int KBUF = BN * L::ROWB;  // bytes per K (or V) tile buffer
-  constexpr int VBUF = KBUF;
-  // wave-wide direct loads (64 lanes x 16 bytes) per tile and tensor, per wave
-  constexpr int NL = (L::SLOTS + NW - 1) / NW;
+  constexpr int KBUF = BN * L::ROWB;  // bytes per K (or V) tile
+  // A tile is NLOADS wave-wide direct loads (64 lanes x 16 bytes); each wave
+  // issues NL of them, and a wave whose last load falls past the tile sends
+  // it, all lanes out of range, into a 1 KB spill slot after the tile, so
+  // the issue code has no branches.
+  constexpr int NLOADS = KBUF / 1024;
+  constexpr int NL = (NLOADS + NW - 1) / NW;
+  constexpr int BUF_BYTES = KBUF + (NL * NW > NLOADS ? 1024 : 0);  // one LDS buffer
+  static_assert(NLOADS * 1024 == KBUF, "a tile is a whole number of wave-wide loads");
 
   // One array per buffer half: the compiler can then tell that a direct
   // load into one half does not feed reads of the other, and does not make
   // those reads wait for the load.
-  __shared__ __attribute__((aligned(1024))) char k_lds0[KBUF];
-  __shared__ __attribute__((aligned(1024))) char k_lds1[KBUF];
-  __shared__ __attribute__((aligned(1024))) char v_lds0[VBUF];
-  __shared__ __attribute__((aligned(1024))) char v_lds1[VBUF];
+  __shared__ __attribute__((aligned(1024))) char k_lds0[BUF_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[BUF_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[BUF_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[BUF_BYTES];
   auto k_buf = [](auto tag) -> char * {
     if constexpr (decltype(tag)::value == 0) return k_lds0; else return k_lds1;
   };
@@ -499,6 +513,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < NW);
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
@@ -521,29 +536,39 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
   row_range(mask, W, q0, n, kv_lo, tmp);
   row_range(mask, W, qend - 1, n, tmp, kv_hi);
 
-  const int wq0 = q0 + wave * 32;
+  // The wave's rows [wq0, wq0 + 32R): the union of their visible keys is
+  // [w_lo, w_hi), the intersection [i_lo, i_hi).
+  const int wq0 = q0 + wave * 32 * R;
   const bool wave_active = wq0 < n;
   int w_lo = 0, w_hi = 0, i_lo = 0, i_hi = 0;
   if (wave_active) {
-    const int wq1 = min(wq0 + 32, n);
+    const int wq1 = min(wq0 + 32 * R, n);
     row_range(mask, W, wq0, n, w_lo, i_hi);
     row_range(mask, W, wq1 - 1, n, i_lo, w_hi);
   }
-  const int row = wq0 + l32;
-  const bool row_ok = row < n;
-  int lo_r = 0, hi_r = 0;
-  if (row_ok) row_range(mask, W, row, n, lo_r, hi_r);
+  // Sub-block r: this lane's query row wq0 + 32r + l32.
+  int row[R], lo_r[R], hi_r[R];
+  bool row_ok[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    row[r] = wq0 + 32 * r + l32;
+    row_ok[r] = row[r] < n;
+    lo_r[r] = 0;
+    hi_r[r] = 0;
+    if (row_ok[r]) row_range(mask, W, row[r], n, lo_r[r], hi_r[r]);
+  }
 
-  // Q fragments (B operand of S^T = K Q^T): lane (l32, g) holds
-  // q[row][16*kk + 8*g .. +7].
-  bf16x8 qf[KST];
-  {
+  // Q fragments (B operand of S^T = K Q^T): lane (l32, g) of sub-block r
+  // holds q[row[r]][16*kk + 8*g .. +7].
+  bf16x8 qf[R][KST];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
     const __bf16 *qrow = reinterpret_cast<const __bf16 *>(a.q) +
-                         ((size_t)(s0 + (row_ok ? row : 0)) * a.hq + h) * D;
+                         ((size_t)(s0 + (row_ok[r] ? row[r] : 0)) * a.hq + h) * D;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk)
-      qf[kk] = row_ok ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * kk + 8 * g)
-                      : (bf16x8)((__bf16)0.0f);
+      qf[r][kk] = row_ok[r] ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * kk + 8 * g)
+                            : (bf16x8)((__bf16)0.0f);
   }
 
   // Direct loads: wave-wide load j fills LDS slots 64j .. 64j+63 of a tile;
@@ -553,23 +578,25 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int p = (wave + NW * i) * 64 + lane;
-    const int r = p / L::SLOTS, cs = p % L::SLOTS;
-    ld_off[i] = cs < CH ? (uint32_t)(r * rowbytes + cs * 16) : kOutOfRange;
+    const int rr = p / L::SLOTS, cs = p % L::SLOTS;
+    ld_off[i] = cs < CH ? (uint32_t)(rr * rowbytes + cs * 16) : kOutOfRange;
   }
   const char *kseq = reinterpret_cast<const char *>(a.k) + ((size_t)s0 * a.hkv + hk) * D * 2;
   const char *vseq = reinterpret_cast<const char *>(a.v) + ((size_t)s0 * a.hkv + hk) * D * 2;
 
   // Direct loads of the K (or V) rows kt .. kt+63 into an LDS buffer.
+  // kt >= kv_hi is allowed: the range is then empty, nothing is fetched and
+  // the (unused) buffer fills with zeros, so a step needs no branch.
   auto issue = [&](const char *seq, char *lds, int kt) {
     const int nrows = min(kv_hi - kt, BN);
-    const int rec = (nrows - 1) * rowbytes + D * 2;  // later rows read as zeros
+    const int rec = max(0, (nrows - 1) * rowbytes + D * 2);  // later rows read as zeros
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char *>(seq + (size_t)kt * rowbytes), (short)0, rec, kBufferWord3);
 #pragma unroll
-    for (int i = 0; i < NL; ++i)
-      if (wave + NW * i < L::SLOTS)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_void_t *)(lds + (wave + NW * i) * 1024), 16, ld_off[i], 0, 0, 0);
+    for (int i = 0; i < NL; ++i) {
+      const int j = min(wave + NW * i, NLOADS);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(lds + j * 1024), 16, ld_off[i], 0, 0, 0);
+    }
   };
   auto issue_k = [&](int kt, auto buf_tag) { issue(kseq, k_buf(buf_tag), kt); };
   auto issue_v = [&](int kt, auto buf_tag) { issue(vseq, v_buf(buf_tag), kt); };
@@ -583,93 +610,108 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
   const int kread = key_of_row(l32) * L::ROWB + 16 * g;
   const int vread = (g + 4 * ((lane & 15) >> 2)) * L::ROWB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
-  f32x16 o[DB];
+  f32x16 o[R][DB];
+  float l_run[R];  // this lane's share of each row sum
+  // Softmax reference of each row in exp2 units, fixed for a whole sweep:
+  // the maximum of the first tile holding keys visible to the row.  Later
+  // keys may score higher, so probabilities exp2(c*s - m) may exceed 1 (fp32
+  // and bf16 keep the same 8 exponent bits, so relative precision is
+  // unchanged) and O is never rescaled.  If a row's sum or output comes out
+  // non-finite (a score more than ~127 doublings above that first maximum),
+  // the workgroup sweeps once more for the exact row maxima and then repeats
+  // the accumulation with them, where no probability exceeds 1.
+  float m_ref[R];
+  auto reset = [&]() {
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = (f32x16)(0.0f);
-  float l_run = 0.0f;  // this lane's share of the row sum
-  // Softmax reference of the row in exp2 units, fixed for a whole sweep: the
-  // maximum of the first tile holding keys visible to the row.  Later keys
-  // may score higher, so probabilities exp2(c*s - m) may exceed 1 (fp32 and
-  // bf16 keep the same 8 exponent bits, so relative precision is unchanged)
-  // and O is never rescaled.  If a row's sum or output comes out non-finite
-  // (a score more than ~127 doublings above that first maximum), the
-  // workgroup sweeps once more for the exact row maximum and then repeats
-  // the accumulation with it, where no probability exceeds 1.
-  float m_ref = row_ok ? kNegInf : 0.0f;
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[r][db] = (f32x16)(0.0f);
+      l_run[r] = 0.0f;
+      m_ref[r] = row_ok[r] ? kNegInf : 0.0f;
+    }
+  };
+  reset();
 
   // accumulator entry j of block nb (lane half g) holds key
   // kt + 32 nb + key_of_row(8 (j >> 2) + 4 g + (j & 3))
-  auto visible = [&](int kt, int nb, int j) {
+  auto visible = [&](int r, int kt, int nb, int j) {
     const int key = kt + nb * 32 + 16 * (j >> 3) + 2 * ((j >> 2) & 1) + 4 * (j & 3) + g;
-    return key >= lo_r && key < hi_r;
+    return key >= lo_r[r] && key < hi_r[r];
   };
   // a score that becomes -inf once multiplied by c
   const float s_void = neg ? __builtin_huge_valf() : kNegInf;
 
-  // S^T = K Q^T for the 64 keys held in K buffer KB.
-  auto qk = [&](auto kbuf_tag, f32x16 (&sc)[2]) {
-    constexpr int KB = decltype(kbuf_tag)::value;
+  // S^T = K Q^T for the 64 keys held in K buffer KB, every sub-block; each K
+  // fragment feeds the R sub-blocks' MFMAs in a row.
+  auto qk = [&](auto kbuf_tag, f32x16 (&sc)[R][2]) {
     const char *kb = k_buf(kbuf_tag) + kread;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      sc[nb] = (f32x16)(0.0f);
+#pragma unroll
+      for (int r = 0; r < R; ++r) sc[r][nb] = (f32x16)(0.0f);
 #pragma unroll
       for (int kk = 0; kk < KST; ++kk) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + nb * 32 * L::ROWB + kk * 32);
-        sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc[nb], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          sc[r][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[r][kk], sc[r][nb], 0, 0, 0);
       }
     }
   };
   // Schedule of a plain tile (one basic block): the MFMAs of the second
   // 32-key block of S^T run under the softmax of the first, and the PV MFMAs
   // of the first two k steps under the softmax of the second, with a few LDS
-  // reads kept ahead of their MFMAs (mask: 2 VALU, 8 MFMA, 0x100 DS read).
+  // reads kept ahead of their MFMAs and the next tile's loads spread over
+  // the first MFMAs (mask: 2 VALU, 8 MFMA, 0x20 VMEM read, 0x100 DS read).
   auto plain_tile_schedule = [&]() {
     constexpr int SOFT = 3 * (BN / 2) / KST;  // softmax VALU ops per QK MFMA
-    constexpr int PV_HALF = DB * (BN / 32);   // PV MFMAs per pair of k steps
+    constexpr int PV_HALF = DB * (BN / 32);   // PV k-step pairs' fragments
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < KST; ++i) {  // S^T block 0
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    for (int i = 0; i < KST; ++i) {  // S^T block 0, with the next tile's loads
+      __builtin_amdgcn_sched_group_barrier(0x008, R, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 2 * NL / KST + 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 #pragma unroll
-    for (int i = 0; i < KST; ++i) {  // S^T block 1 under softmax of block 0
+    for (int i = 0; i < KST * R; ++i) {  // S^T block 1 under softmax of block 0
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, SOFT, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (i % R == R - 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
 #pragma unroll
-    for (int i = 0; i < PV_HALF; ++i) {  // PV of k steps 0-1 under softmax of block 1
+    for (int i = 0; i < PV_HALF * R; ++i) {  // PV of k steps 0-1 under softmax of block 1
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 2 * KST * SOFT / PV_HALF, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (i % R == R - 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
 #pragma unroll
-    for (int i = 0; i < PV_HALF; ++i) {  // PV of k steps 2-3
+    for (int i = 0; i < PV_HALF * R; ++i) {  // PV of k steps 2-3
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (i % R == R - 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
-  auto apply_mask = [&](f32x16 (&sc)[2], int kt) {
+  auto apply_mask = [&](f32x16 (&sc)[R][2], int kt) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sc[nb][j] = visible(kt, nb, j) ? sc[nb][j] : s_void;
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sc[r][nb][j] = visible(r, kt, nb, j) ? sc[r][nb][j] : s_void;
   };
-  // Row maximum of c*s over the tile, both lane halves combined.
-  auto row_max = [&](const f32x16 (&sc)[2]) {
+  // Row maximum of c*s over the tile for sub-block r, both lane halves combined.
+  auto row_max = [&](const f32x16 (&scr)[2]) {
     float mx = kNegInf;
     if (neg) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, -sc[nb][j]);
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, -scr[nb][j]);
     } else {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[nb][j]);
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, scr[nb][j]);
     }
     const float mt = mx * cabs;
     return fmaxf(mt, xor32(mt));
@@ -678,25 +720,27 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
   // of those same bf16 values.  k step ks covers keys 16ks .. 16ks+15, held
   // in accumulator entries 8*(ks&1) .. +7 of block ks>>1; entry e of lane
   // half g is key 16ks + g + 4(e & 3) + 2(e >> 2).
-  auto softmax = [&](f32x16 (&sc)[2], bf16x8 (&pf)[BN / 16]) {
-    // a row with no visible key yet has every score at -inf here
-    const float neg_m = m_ref == kNegInf ? 0.0f : -m_ref;
+  auto softmax = [&](f32x16 (&sc)[R][2], bf16x8 (&pf)[R][BN / 16]) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int ks = 0; ks < BN / 16; ++ks) {
+    for (int ks = 0; ks < BN / 16; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pf[ks][e] = (__bf16)fast_exp2(__builtin_fmaf(sc[ks >> 1][8 * (ks & 1) + e], c, neg_m));
+      for (int r = 0; r < R; ++r) {
+        // a row with no visible key yet has every score at -inf here
+        const float neg_m = m_ref[r] == kNegInf ? 0.0f : -m_ref[r];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16x2 pr = {pf[ks][2 * e], pf[ks][2 * e + 1]};
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+        for (int e = 0; e < 8; ++e)
+          pf[r][ks][e] = (__bf16)fast_exp2(__builtin_fmaf(sc[r][ks >> 1][8 * (ks & 1) + e], c, neg_m));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 pr = {pf[r][ks][2 * e], pf[r][ks][2 * e + 1]};
+          l_run[r] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run[r], false);
+        }
       }
-    }
   };
-  // O += P V with V from V buffer VB.
-  auto pv = [&](auto vbuf_tag, const bf16x8 (&pf)[BN / 16]) {
-    constexpr int VB = decltype(vbuf_tag)::value;
+  // O += P V with V from V buffer VB; each V fragment feeds the R
+  // sub-blocks' MFMAs in a row.
+  auto pv = [&](auto vbuf_tag, const bf16x8 (&pf)[R][BN / 16]) {
     const char *vb = v_buf(vbuf_tag) + vread;
 #pragma unroll
     for (int ks = 0; ks < BN / 16; ++ks)
@@ -707,7 +751,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp + 2 * L::ROWB));
         const bf16x8 vf = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          o[r][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[r][ks], o[r][db], 0, 0, 0);
       }
   };
 
@@ -736,12 +782,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
       t_plain1 = last;
     }
   }
+
+  // General step (first tile, diagonal and edge tiles): a wave that sees
+  // none of the tile only joins the barrier; otherwise masking and the
+  // reference update touch only S and m_ref, then the same softmax and PV run.
   auto k_rt = [&](int buf) -> const char * { return buf ? k_lds1 : k_lds0; };
   auto v_rt = [&](int buf) -> const char * { return buf ? v_lds1 : v_lds0; };
-
-  // General step (first tile, diagonal and edge tiles): scores of a tile the
-  // wave does not see are voided (P = 0); masking and the reference update
-  // touch only S and m_ref, then the same softmax and PV run.
   auto general_step = [&](int t) __attribute__((always_inline)) {
     const int kt = kv_lo + t * BN;
     const int buf = t & 1;
@@ -754,45 +800,49 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
         issue_v(kt + BN, std::integral_constant<int, 1>{});
       }
     }
-    f32x16 sc[2];
-    {
-      const char *kb = k_rt(buf) + kread;
+    if (wave_sees(t)) {
+      f32x16 sc[R][2];
+      {
+        const char *kb = k_rt(buf) + kread;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        sc[nb] = (f32x16)(0.0f);
+        for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-        for (int kk = 0; kk < KST; ++kk) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + nb * 32 * L::ROWB + kk * 32);
-          sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc[nb], 0, 0, 0);
+          for (int r = 0; r < R; ++r) sc[r][nb] = (f32x16)(0.0f);
+#pragma unroll
+          for (int kk = 0; kk < KST; ++kk) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + nb * 32 * L::ROWB + kk * 32);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+              sc[r][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[r][kk], sc[r][nb], 0, 0, 0);
+          }
         }
       }
-    }
-    if (!wave_sees(t)) {
+      if (needs_mask(t)) apply_mask(sc, kt);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) sc[nb] = (f32x16)(s_void);
-    } else if (needs_mask(t)) {
-      apply_mask(sc, kt);
-    }
-    if (__builtin_amdgcn_ballot_w64(m_ref == kNegInf)) {
-      const float mt = row_max(sc);
-      m_ref = m_ref == kNegInf ? mt : m_ref;
-    }
-    bf16x8 pf[BN / 16];
-    softmax(sc, pf);
-    {
-      const char *vb = v_rt(buf) + vread;
-#pragma unroll
-      for (int ks = 0; ks < BN / 16; ++ks)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const char *vp = vb + ks * 16 * L::ROWB + db * 64;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp));
-          const i16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp + 2 * L::ROWB));
-          const bf16x8 vf = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
+      for (int r = 0; r < R; ++r)
+        if (__builtin_amdgcn_ballot_w64(m_ref[r] == kNegInf)) {
+          const float mt = row_max(sc[r]);
+          m_ref[r] = m_ref[r] == kNegInf ? mt : m_ref[r];
         }
+      bf16x8 pf[R][BN / 16];
+      softmax(sc, pf);
+      {
+        const char *vb = v_rt(buf) + vread;
+#pragma unroll
+        for (int ks = 0; ks < BN / 16; ++ks)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const char *vp = vb + ks * 16 * L::ROWB + db * 64;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp));
+            const i16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp + 2 * L::ROWB));
+            const bf16x8 vf = __builtin_bit_cast(
+                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+              o[r][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[r][ks], o[r][db], 0, 0, 0);
+          }
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -801,12 +851,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
   auto plain_step = [&](auto buf_tag, int t) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value;
     const int kt = kv_lo + t * BN;
-    if (t + 1 < ntiles) {
-      issue_k(kt + BN, std::integral_constant<int, BUF ^ 1>{});
-      issue_v(kt + BN, std::integral_constant<int, BUF ^ 1>{});
-    }
-    f32x16 sc[2];
-    bf16x8 pf[BN / 16];
+    // the last tile's "next" loads are empty (range starts at kv_hi)
+    const int kn = min(kt + BN, kv_hi);
+    issue_k(kn, std::integral_constant<int, BUF ^ 1>{});
+    issue_v(kn, std::integral_constant<int, BUF ^ 1>{});
+    f32x16 sc[R][2];
+    bf16x8 pf[R][BN / 16];
     qk(buf_tag, sc);
     softmax(sc, pf);
     pv(buf_tag, pf);
@@ -836,12 +886,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
     auto step = [&](auto buf_tag, int t) {
       constexpr int BUF = decltype(buf_tag)::value;
       const int kt = kv_lo + t * BN;
-      if (t + 1 < ntiles) issue_k(kt + BN, std::integral_constant<int, BUF ^ 1>{});
+      issue_k(min(kt + BN, kv_hi), std::integral_constant<int, BUF ^ 1>{});
       if (wave_sees(t)) {
-        f32x16 sc[2];
+        f32x16 sc[R][2];
         qk(buf_tag, sc);
         if (needs_mask(t)) apply_mask(sc, kt);
-        m_ref = fmaxf(m_ref, row_max(sc));
+#pragma unroll
+        for (int r = 0; r < R; ++r) m_ref[r] = fmaxf(m_ref[r], row_max(sc[r]));
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -862,36 +913,39 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_fast(const LaunchArgs a) 
     // with the exact row maxima as references.
     bool bad = false;
     if (wave_active) {
-      const float l_tot = l_run + xor32(l_run);
-      bad = row_ok && !__builtin_isfinite(l_tot);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int r = 0; r < R; ++r) {
+        const float l_tot = l_run[r] + xor32(l_run[r]);
+        bad = bad || (row_ok[r] && !__builtin_isfinite(l_tot));
 #pragma unroll
-        for (int j = 0; j < 16; ++j) bad = bad || (row_ok && !__builtin_isfinite(o[db][j]));
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) bad = bad || (row_ok[r] && !__builtin_isfinite(o[r][db][j]));
+      }
     }
     if (!__syncthreads_or(bad)) break;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] = (f32x16)(0.0f);
-    l_run = 0.0f;
-    m_ref = row_ok ? kNegInf : 0.0f;
+    reset();
     max_sweep();
   }
 
   if (wave_active) {
-    const float l_tot = l_run + xor32(l_run);
-    if (row_ok) {
-      const float inv = 1.0f / l_tot;
-      __bf16 *orow = reinterpret_cast<__bf16 *>(a.out) + ((size_t)(s0 + row) * a.hq + h) * D;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int r = 0; r < R; ++r) {
+      const float l_tot = l_run[r] + xor32(l_run[r]);
+      if (row_ok[r]) {
+        const float inv = 1.0f / l_tot;
+        __bf16 *orow = reinterpret_cast<__bf16 *>(a.out) + ((size_t)(s0 + row[r]) * a.hq + h) * D;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int d = 32 * db + 8 * jj + 4 * g;
-          bf16x4 w;
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * jj + e] * inv);
-          *reinterpret_cast<bf16x4 *>(orow + d) = w;
-        }
+          for (int jj = 0; jj < 4; ++jj) {
+            const int d = 32 * db + 8 * jj + 4 * g;
+            bf16x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[r][db][4 * jj + e] * inv);
+            *reinterpret_cast<bf16x4 *>(orow + d) = w;
+          }
+      }
     }
   }
 #endif  // __HIP_DEVICE_COMPILE__
@@ -1048,9 +1102,9 @@ int rows_per_workgroup_f32(int) { return 128; }
 
 int launch_bf16(const LaunchArgs &a, int head_dim, void *stream) {
   switch (head_dim) {
-    case 64: return launch(fwd_bf16_fast<64, kWavesBf16>, a, kWavesBf16 * 64, stream);
+    case 64: return launch(fwd_bf16_fast<64, kWavesBf16, 1>, a, kWavesBf16 * 64, stream);
     case 72: return launch(fwd_bf16_generic<72, kWavesBf16>, a, kWavesBf16 * 64, stream);
-    case 128: return launch(fwd_bf16_fast<128, kWavesBf16>, a, kWavesBf16 * 64, stream);
+    case 128: return launch(fwd_bf16_fast<128, kWavesBf16, 1>, a, kWavesBf16 * 64, stream);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
 }

@@ -34,6 +34,11 @@ struct LaunchArgs {
   int32_t seq_start[kMaxSeqsPerLaunch];  // packed index of token 0
   int32_t seq_len[kMaxSeqsPerLaunch];    // tokens
   int32_t seq_tiles[kMaxSeqsPerLaunch];  // ceil(len / bm), non-increasing
+  // Causal order only (items by query-tile level, heaviest first): query-tile
+  // levels m in [seq_tiles[k], seq_tiles[k-1]) hold the k longest sequences,
+  // and their items start at level_start[k-1]; level_start[n_seqs] =
+  // total_items (seq_tiles[n_seqs] reads as 0).
+  int32_t level_start[kMaxSeqsPerLaunch + 1];
 };
 
 // Kernel families.  Each returns 0 or a hipError_t value.
