@@ -13,6 +13,11 @@ result (iii); gist.science technical summary, Metodologia, attention rewrite).
 
 Mask specifications accepted here: ``"causal"``, ``"full"`` or
 ``("window", W)`` with W > 0.
+
+``cu_seqlens_k`` (optional, on ``attention`` and ``attention_rows``): the
+keys/values have their own packing, sequence b holding Lk_b >= Lq_b tokens,
+and its Lq_b queries are the last Lq_b positions of the sequence (query i at
+position i + Lk_b - Lq_b).
 """
 from __future__ import annotations
 
@@ -51,6 +56,12 @@ def _bind(path: str) -> ctypes.CDLL:
     lib.oracle_attention_probs.argtypes = [dp, dp, dp, ip, i32, i32, i32, i32, i32, i32,
                                            ctypes.c_double, ctypes.c_int64, i32, dp]
     lib.oracle_attention_probs.restype = ctypes.c_int64
+    lib.oracle_attention_kv.argtypes = [dp, dp, dp, ip, ip, i32, i32, i32, i32, i32, i32,
+                                        ctypes.c_double, dp, dp]
+    lib.oracle_attention_kv.restype = ctypes.c_int
+    lib.oracle_attention_kv_rows.argtypes = [dp, dp, dp, ip, ip, i32, i32, i32, i32, i32, i32,
+                                             ctypes.c_double, lp, ip, ctypes.c_int64, dp, dp]
+    lib.oracle_attention_kv_rows.restype = ctypes.c_int
     return lib
 
 
@@ -93,35 +104,40 @@ class Oracle:
         self._lib = lib
 
     @staticmethod
-    def _prep(q, k, v, cu_seqlens):
+    def _prep(q, k, v, cu_seqlens, cu_seqlens_k=None):
         q, k, v = _f64(q), _f64(k), _f64(v)
         cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        cu_k = cu if cu_seqlens_k is None else np.ascontiguousarray(
+            np.asarray(cu_seqlens_k, dtype=np.int32))
         if q.ndim != 3 or k.ndim != 3 or v.shape != k.shape:
-            raise ValueError("q must be [T,Hq,d]; k and v [T,Hkv,d]")
+            raise ValueError("q must be [Tq,Hq,d]; k and v [Tk,Hkv,d]")
         T, hq, d = q.shape
-        if k.shape[0] != T or k.shape[2] != d:
-            raise ValueError("q, k, v disagree on T or d")
+        if k.shape[2] != d:
+            raise ValueError("q, k, v disagree on d")
         if cu.ndim != 1 or cu.size < 1 or int(cu[-1]) != T:
-            raise ValueError("cu_seqlens must end at T")
-        return q, k, v, cu, T, hq, k.shape[1], d
+            raise ValueError("cu_seqlens must end at Tq")
+        if cu_k.shape != cu.shape or int(cu_k[-1]) != k.shape[0]:
+            raise ValueError("cu_seqlens_k must have n_seqs+1 entries and end at Tk")
+        return q, k, v, cu, cu_k, T, hq, k.shape[1], d
 
-    def attention(self, q, k, v, cu_seqlens, mask, scale, return_lse=False):
-        """Every output row, fp64 [T, Hq, d] (and the log-sum-exp [T, Hq])."""
-        q, k, v, cu, T, hq, hkv, d = self._prep(q, k, v, cu_seqlens)
+    def attention(self, q, k, v, cu_seqlens, mask, scale, return_lse=False, cu_seqlens_k=None):
+        """Every output row, fp64 [Tq, Hq, d] (and the log-sum-exp [Tq, Hq])."""
+        q, k, v, cu, cu_k, T, hq, hkv, d = self._prep(q, k, v, cu_seqlens, cu_seqlens_k)
         code, w = _mask(mask)
         out = np.zeros((T, hq, d), dtype=np.float64)
         lse = np.zeros((T, hq), dtype=np.float64)
-        rc = self._lib.oracle_attention(
+        rc = self._lib.oracle_attention_kv(
             _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
-            _ptr(cu, ctypes.c_int32), cu.size - 1, hq, hkv, d, code, w, float(scale),
-            _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
+            _ptr(cu, ctypes.c_int32), _ptr(cu_k, ctypes.c_int32), cu.size - 1, hq, hkv, d,
+            code, w, float(scale), _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
         if rc != 0:
             raise ValueError("oracle rejected its arguments")
         return (out, lse) if return_lse else out
 
-    def attention_rows(self, q, k, v, cu_seqlens, mask, scale, rows, heads, return_lse=False):
-        """Selected rows: out[r] is packed token rows[r], query head heads[r]."""
-        q, k, v, cu, T, hq, hkv, d = self._prep(q, k, v, cu_seqlens)
+    def attention_rows(self, q, k, v, cu_seqlens, mask, scale, rows, heads, return_lse=False,
+                       cu_seqlens_k=None):
+        """Selected rows: out[r] is packed query token rows[r], query head heads[r]."""
+        q, k, v, cu, cu_k, T, hq, hkv, d = self._prep(q, k, v, cu_seqlens, cu_seqlens_k)
         code, w = _mask(mask)
         rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
         heads = np.ascontiguousarray(np.asarray(heads, dtype=np.int32))
@@ -129,18 +145,18 @@ class Oracle:
             raise ValueError("rows and heads must be 1-D and equal in length")
         out = np.zeros((rows.size, d), dtype=np.float64)
         lse = np.zeros(rows.size, dtype=np.float64)
-        rc = self._lib.oracle_attention_rows(
+        rc = self._lib.oracle_attention_kv_rows(
             _ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
-            _ptr(cu, ctypes.c_int32), cu.size - 1, hq, hkv, d, code, w, float(scale),
-            _ptr(rows, ctypes.c_int64), _ptr(heads, ctypes.c_int32), rows.size,
-            _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
+            _ptr(cu, ctypes.c_int32), _ptr(cu_k, ctypes.c_int32), cu.size - 1, hq, hkv, d,
+            code, w, float(scale), _ptr(rows, ctypes.c_int64), _ptr(heads, ctypes.c_int32),
+            rows.size, _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double))
         if rc != 0:
             raise ValueError("oracle rejected its arguments")
         return (out, lse) if return_lse else out
 
     def probs(self, q, k, v, cu_seqlens, mask, scale, t, h):
         """Softmax weights of row (t, h) over its sequence's keys (0 where invisible)."""
-        q, k, v, cu, T, hq, hkv, d = self._prep(q, k, v, cu_seqlens)
+        q, k, v, cu, _, T, hq, hkv, d = self._prep(q, k, v, cu_seqlens)
         code, w = _mask(mask)
         b = int(np.searchsorted(cu, t, side="right") - 1)
         while b + 1 < cu.size and cu[b + 1] <= t:

@@ -37,6 +37,17 @@
  * Layout: q[T][Hq][d], k[T][Hkv][d], v[T][Hkv][d], row-major fp64, T the
  * total number of packed tokens; cu_seqlens[n_seqs+1] gives sequence b the
  * tokens cu_seqlens[b] .. cu_seqlens[b+1]-1.
+ *
+ * Queries against a longer key sequence (the *_kv entry points).  The
+ * document pages keep the key/value cache resident on the GPU and run
+ * prefill and then decode over it (gist.science technical summary, KV cache
+ * and decode figures), so a call may hold fewer new queries than keys:
+ * q[Tq][Hq][d] packed by cu_q, k/v[Tk][Hkv][d] packed by cu_k, with
+ * Lq_b = cu_q[b+1]-cu_q[b] <= Lk_b = cu_k[b+1]-cu_k[b].  The pages do not say
+ * where those queries sit; the plain reading is that they are the LAST Lq_b
+ * tokens of the sequence (the newest tokens, "bottom-right" alignment), so
+ * local query i has position p = i + Lk_b - Lq_b and every mask above is
+ * evaluated at p over Lk_b keys.  With cu_q = cu_k this is the square case.
  */
 #include <math.h>
 #include <stdint.h>
@@ -72,29 +83,25 @@ static int seq_of_token(const int32_t *cu, int n_seqs, int64_t t) {
 }
 
 /*
- * One output row: token t (packed index), query head h.  Writes d values to
- * out_row, and, when lse is non-NULL, log(sum_j exp(s_j)) to *lse.  When
- * probs is non-NULL it receives the softmax weights of the visible keys, in
- * key order (the caller sizes it to the sequence length).  Returns the
- * number of visible keys.
+ * One output row: the query row qi of query head h at position pos of a
+ * sequence whose n keys/values start at kseq/vseq.  Writes d values to
+ * out_row and, when lse is non-NULL, log(sum_j exp(s_j)) to *lse.  When probs
+ * is non-NULL it receives the softmax weights of the visible keys, in key
+ * order (the caller sizes it to the sequence length).  Returns the number of
+ * visible keys.
  */
-static int64_t one_row(const double *q, const double *k, const double *v,
-                       const int32_t *cu, int n_seqs, int hq, int hkv, int d,
-                       int mask, int64_t window, double scale, int64_t t,
-                       int h, double *out_row, double *lse, double *probs,
+static int64_t one_row(const double *qi, const double *kseq, const double *vseq,
+                       int hq, int hkv, int d, int mask, int64_t window,
+                       double scale, int64_t pos, int64_t n, int h,
+                       double *out_row, double *lse, double *probs,
                        double *scores) {
-    int b = seq_of_token(cu, n_seqs, t);
-    int64_t s0 = cu[b];
-    int64_t n = (int64_t)cu[b + 1] - s0;
-    int64_t i = t - s0;
     int g = h / (hq / hkv);
     int64_t lo, hi;
-    visible_range(mask, window, i, n, &lo, &hi);
+    visible_range(mask, window, pos, n, &lo, &hi);
 
-    const double *qi = q + ((size_t)t * hq + h) * d;
     /* scores of the visible keys */
     for (int64_t j = lo; j < hi; j++) {
-        const double *kj = k + ((size_t)(s0 + j) * hkv + g) * d;
+        const double *kj = kseq + ((size_t)j * hkv + g) * d;
         double dot = 0.0;
         for (int c = 0; c < d; c++) dot += qi[c] * kj[c];
         scores[j - lo] = scale * dot;
@@ -112,7 +119,7 @@ static int64_t one_row(const double *q, const double *k, const double *v,
     for (int c = 0; c < d; c++) out_row[c] = 0.0;
     for (int64_t j = lo; j < hi; j++) {
         double p = scores[j - lo] / l;
-        const double *vj = v + ((size_t)(s0 + j) * hkv + g) * d;
+        const double *vj = vseq + ((size_t)j * hkv + g) * d;
         for (int c = 0; c < d; c++) out_row[c] += p * vj[c];
         if (probs) probs[j - lo] = p;
     }
@@ -120,36 +127,62 @@ static int64_t one_row(const double *q, const double *k, const double *v,
     return hi - lo;
 }
 
-static int args_ok(const int32_t *cu, int n_seqs, int hq, int hkv, int d,
-                   int mask, int64_t window) {
+/* Row of packed query token t (head h): locate its sequence and position. */
+static int64_t token_row(const double *q, const double *k, const double *v,
+                         const int32_t *cu_q, const int32_t *cu_k, int n_seqs,
+                         int hq, int hkv, int d, int mask, int64_t window,
+                         double scale, int64_t t, int h, double *out_row,
+                         double *lse, double *probs, double *scores) {
+    int b = seq_of_token(cu_q, n_seqs, t);
+    int64_t lq = (int64_t)cu_q[b + 1] - cu_q[b];
+    int64_t lk = (int64_t)cu_k[b + 1] - cu_k[b];
+    int64_t pos = (t - cu_q[b]) + (lk - lq);
+    const double *kseq = k + (size_t)cu_k[b] * hkv * d;
+    const double *vseq = v + (size_t)cu_k[b] * hkv * d;
+    return one_row(q + ((size_t)t * hq + h) * d, kseq, vseq, hq, hkv, d, mask,
+                   window, scale, pos, lk, h, out_row, lse, probs, scores);
+}
+
+static int args_ok(const int32_t *cu_q, const int32_t *cu_k, int n_seqs,
+                   int hq, int hkv, int d, int mask, int64_t window) {
     if (n_seqs < 0 || hq <= 0 || hkv <= 0 || d <= 0) return 0;
     if (hq % hkv != 0) return 0;
     if (mask != ORACLE_MASK_CAUSAL && mask != ORACLE_MASK_FULL &&
         mask != ORACLE_MASK_WINDOW)
         return 0;
     if (mask == ORACLE_MASK_WINDOW && window <= 0) return 0;
-    if (n_seqs > 0 && cu[0] != 0) return 0;
-    for (int b = 0; b < n_seqs; b++)
-        if (cu[b + 1] < cu[b]) return 0;
+    if (n_seqs > 0 && (cu_q[0] != 0 || cu_k[0] != 0)) return 0;
+    for (int b = 0; b < n_seqs; b++) {
+        if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b]) return 0;
+        /* queries are the last Lq tokens of a sequence of Lk */
+        if (cu_q[b + 1] - cu_q[b] > cu_k[b + 1] - cu_k[b]) return 0;
+    }
     return 1;
 }
 
-/*
- * Selected rows: row r is packed token rows[r], query head heads[r].
- * out is [n_rows][d]; lse (optional) is [n_rows].  Returns 0, or -1 on bad
- * arguments or a row index outside [0, T).
- */
-int oracle_attention_rows(const double *q, const double *k, const double *v,
-                          const int32_t *cu, int32_t n_seqs, int32_t hq,
-                          int32_t hkv, int32_t d, int32_t mask, int32_t window,
-                          double scale, const int64_t *rows,
-                          const int32_t *heads, int64_t n_rows, double *out,
-                          double *lse) {
-    if (!args_ok(cu, n_seqs, hq, hkv, d, mask, window)) return -1;
-    int64_t T = n_seqs > 0 ? cu[n_seqs] : 0;
-    int64_t maxlen = 0;
+static int64_t max_len(const int32_t *cu, int n_seqs) {
+    int64_t m = 0;
     for (int b = 0; b < n_seqs; b++)
-        if (cu[b + 1] - cu[b] > maxlen) maxlen = cu[b + 1] - cu[b];
+        if (cu[b + 1] - cu[b] > m) m = cu[b + 1] - cu[b];
+    return m;
+}
+
+/*
+ * Selected rows, queries against a key sequence of their own packing: row r
+ * is packed query token rows[r], query head heads[r].  out is [n_rows][d];
+ * lse (optional) is [n_rows].  Returns 0, or -1 on bad arguments or a row
+ * index outside [0, Tq).
+ */
+int oracle_attention_kv_rows(const double *q, const double *k,
+                             const double *v, const int32_t *cu_q,
+                             const int32_t *cu_k, int32_t n_seqs, int32_t hq,
+                             int32_t hkv, int32_t d, int32_t mask,
+                             int32_t window, double scale, const int64_t *rows,
+                             const int32_t *heads, int64_t n_rows, double *out,
+                             double *lse) {
+    if (!args_ok(cu_q, cu_k, n_seqs, hq, hkv, d, mask, window)) return -1;
+    int64_t T = n_seqs > 0 ? cu_q[n_seqs] : 0;
+    int64_t maxlen = max_len(cu_k, n_seqs);
     for (int64_t r = 0; r < n_rows; r++)
         if (rows[r] < 0 || rows[r] >= T || heads[r] < 0 || heads[r] >= hq)
             return -1;
@@ -166,24 +199,23 @@ int oracle_attention_rows(const double *q, const double *k, const double *v,
 #pragma omp for schedule(dynamic, 16)
         for (int64_t r = 0; r < n_rows; r++)
             if (scores)
-                one_row(q, k, v, cu, n_seqs, hq, hkv, d, mask, window, scale,
-                        rows[r], heads[r], out + (size_t)r * d,
-                        lse ? lse + r : NULL, NULL, scores);
+                token_row(q, k, v, cu_q, cu_k, n_seqs, hq, hkv, d, mask, window,
+                          scale, rows[r], heads[r], out + (size_t)r * d,
+                          lse ? lse + r : NULL, NULL, scores);
         free(scores);
     }
     return bad ? -1 : 0;
 }
 
-/* Every row: out is [T][Hq][d], lse (optional) is [T][Hq]. */
-int oracle_attention(const double *q, const double *k, const double *v,
-                     const int32_t *cu, int32_t n_seqs, int32_t hq,
-                     int32_t hkv, int32_t d, int32_t mask, int32_t window,
-                     double scale, double *out, double *lse) {
-    if (!args_ok(cu, n_seqs, hq, hkv, d, mask, window)) return -1;
-    int64_t T = n_seqs > 0 ? cu[n_seqs] : 0;
-    int64_t maxlen = 0;
-    for (int b = 0; b < n_seqs; b++)
-        if (cu[b + 1] - cu[b] > maxlen) maxlen = cu[b + 1] - cu[b];
+/* Every query row: out is [Tq][Hq][d], lse (optional) is [Tq][Hq]. */
+int oracle_attention_kv(const double *q, const double *k, const double *v,
+                        const int32_t *cu_q, const int32_t *cu_k,
+                        int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d,
+                        int32_t mask, int32_t window, double scale,
+                        double *out, double *lse) {
+    if (!args_ok(cu_q, cu_k, n_seqs, hq, hkv, d, mask, window)) return -1;
+    int64_t T = n_seqs > 0 ? cu_q[n_seqs] : 0;
+    int64_t maxlen = max_len(cu_k, n_seqs);
     int bad = 0;
 #pragma omp parallel
     {
@@ -197,12 +229,34 @@ int oracle_attention(const double *q, const double *k, const double *v,
             if (!scores) continue;
             int64_t t = r / hq;
             int h = (int)(r % hq);
-            one_row(q, k, v, cu, n_seqs, hq, hkv, d, mask, window, scale, t,
-                    h, out + (size_t)r * d, lse ? lse + r : NULL, NULL, scores);
+            token_row(q, k, v, cu_q, cu_k, n_seqs, hq, hkv, d, mask, window,
+                      scale, t, h, out + (size_t)r * d, lse ? lse + r : NULL,
+                      NULL, scores);
         }
         free(scores);
     }
     return bad ? -1 : 0;
+}
+
+/* The square case (queries and keys share cu_seqlens): selected rows. */
+int oracle_attention_rows(const double *q, const double *k, const double *v,
+                          const int32_t *cu, int32_t n_seqs, int32_t hq,
+                          int32_t hkv, int32_t d, int32_t mask, int32_t window,
+                          double scale, const int64_t *rows,
+                          const int32_t *heads, int64_t n_rows, double *out,
+                          double *lse) {
+    return oracle_attention_kv_rows(q, k, v, cu, cu, n_seqs, hq, hkv, d, mask,
+                                    window, scale, rows, heads, n_rows, out,
+                                    lse);
+}
+
+/* The square case: every row, out [T][Hq][d], lse (optional) [T][Hq]. */
+int oracle_attention(const double *q, const double *k, const double *v,
+                     const int32_t *cu, int32_t n_seqs, int32_t hq,
+                     int32_t hkv, int32_t d, int32_t mask, int32_t window,
+                     double scale, double *out, double *lse) {
+    return oracle_attention_kv(q, k, v, cu, cu, n_seqs, hq, hkv, d, mask,
+                               window, scale, out, lse);
 }
 
 /*
@@ -216,7 +270,7 @@ int64_t oracle_attention_probs(const double *q, const double *k,
                                int32_t d, int32_t mask, int32_t window,
                                double scale, int64_t t, int32_t h,
                                double *probs) {
-    if (!args_ok(cu, n_seqs, hq, hkv, d, mask, window)) return -1;
+    if (!args_ok(cu, cu, n_seqs, hq, hkv, d, mask, window)) return -1;
     int64_t T = n_seqs > 0 ? cu[n_seqs] : 0;
     if (t < 0 || t >= T || h < 0 || h >= hq) return -1;
     int b = seq_of_token(cu, n_seqs, t);
@@ -232,8 +286,8 @@ int64_t oracle_attention_probs(const double *q, const double *k,
         free(vis);
         return -1;
     }
-    int64_t cnt = one_row(q, k, v, cu, n_seqs, hq, hkv, d, mask, window, scale,
-                          t, h, row, NULL, vis, scores);
+    int64_t cnt = token_row(q, k, v, cu, cu, n_seqs, hq, hkv, d, mask, window,
+                            scale, t, h, row, NULL, vis, scores);
     for (int64_t j = 0; j < n; j++) probs[j] = 0.0;
     for (int64_t j = lo; j < hi; j++) probs[j] = vis[j - lo];
     free(scores);

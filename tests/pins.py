@@ -333,6 +333,112 @@ def pin_dense_bruteforce(orc):
 
 
 # ---------------------------------------------------------------------------
+# 4b. queries against a longer key sequence (chunked prefill, decode): the
+# Lq queries of a sequence are its last Lq positions, query i at i + Lk - Lq
+# ---------------------------------------------------------------------------
+
+def visible_set_kv(mask, i, lq, lk):
+    """Visible keys of local query i when Lq queries end a sequence of Lk keys,
+    as an explicit set (the position offset written out independently)."""
+    pos = i + (lk - lq)
+    if mask == "causal":
+        return {j for j in range(lk) if j <= pos}
+    if mask == "full":
+        return set(range(lk))
+    _, w = mask
+    return {j for j in range(lk) if j // w == pos // w}
+
+
+def _rand_kv(cu_q, cu_k, hq, hkv, d, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (rng.standard_normal((int(cu_q[-1]), hq, d)), rng.standard_normal((int(cu_k[-1]), hkv, d)),
+            rng.standard_normal((int(cu_k[-1]), hkv, d)))
+
+
+KV_CASES = [
+    ([0, 5, 5, 12], [0, 21, 30, 50], 4, 2, 8),    # chunks of 5 and 7 queries, an empty chunk
+    ([0, 1, 2, 3], [0, 17, 18, 40], 2, 1, 16),    # decode: one query per sequence
+    ([0, 9], [0, 9], 2, 2, 4),                    # the square case
+]
+
+
+def pin_kv_torch_sdpa(orc):
+    """torch SDPA (CPU, float64) with an explicit boolean mask built from
+    visible_set_kv, and scipy's logsumexp for the LSE."""
+    import torch
+    import torch.nn.functional as F
+    from scipy.special import logsumexp
+
+    for seed, (cu_q, cu_k, hq, hkv, d) in enumerate(KV_CASES):
+        q, k, v = _rand_kv(cu_q, cu_k, hq, hkv, d, 300 + seed)
+        for mask in MASKS:
+            scale = 0.7 / math.sqrt(d)
+            got, lse = orc.attention(q, k, v, cu_q, mask, scale, return_lse=True, cu_seqlens_k=cu_k)
+            for b in range(len(cu_q) - 1):
+                sq, lq = cu_q[b], cu_q[b + 1] - cu_q[b]
+                sk, lk = cu_k[b], cu_k[b + 1] - cu_k[b]
+                if lq == 0:
+                    continue
+                allowed = torch.tensor([[j in visible_set_kv(mask, i, lq, lk) for j in range(lk)]
+                                        for i in range(lq)])
+                G = hq // hkv
+                tq = torch.from_numpy(q[sq:sq + lq]).permute(1, 0, 2)
+                tk = torch.from_numpy(k[sk:sk + lk]).permute(1, 0, 2).repeat_interleave(G, dim=0)
+                tv = torch.from_numpy(v[sk:sk + lk]).permute(1, 0, 2).repeat_interleave(G, dim=0)
+                o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=allowed, scale=scale)
+                _close(got[sq:sq + lq], o.permute(1, 0, 2).numpy(), 1e-12, f"kv sdpa {cu_q} {cu_k} {mask}")
+                for i in range(lq):
+                    vis = sorted(visible_set_kv(mask, i, lq, lk))
+                    for h in range(hq):
+                        sc = [scale * float(q[sq + i, h] @ k[sk + j, h // G]) for j in vis]
+                        assert abs(lse[sq + i, h] - logsumexp(sc)) < 1e-12, (mask, b, i, h)
+
+
+def pin_kv_suffix_of_square(orc):
+    """Lq queries ending a sequence of Lk give exactly the last Lq rows of the
+    square attention over the whole sequence."""
+    cu_k = [0, 30, 30, 71]
+    q_full, k, v = _rand(cu_k, 4, 2, 6, 31)
+    lqs = [11, 0, 41]
+    cu_q = [0, 11, 11, 52]
+    rows = np.concatenate([np.arange(cu_k[b + 1] - lqs[b], cu_k[b + 1]) for b in range(3)])
+    for mask in MASKS:
+        square = orc.attention(q_full, k, v, cu_k, mask, 0.4)
+        part = orc.attention(q_full[rows], k, v, cu_q, mask, 0.4, cu_seqlens_k=cu_k)
+        _close(part, square[rows], 0.0, f"suffix {mask}")
+
+
+def pin_kv_decode_single_query(orc):
+    """One query per sequence under the causal mask sees every key of its
+    sequence: numpy softmax over all of them."""
+    cu_q, cu_k = [0, 1, 2], [0, 13, 40]
+    q, k, v = _rand_kv(cu_q, cu_k, 4, 1, 8, 32)
+    got = orc.attention(q, k, v, cu_q, "causal", 0.5, cu_seqlens_k=cu_k)
+    for b in range(2):
+        ks, vs = k[cu_k[b]:cu_k[b + 1], 0], v[cu_k[b]:cu_k[b + 1], 0]
+        for h in range(4):
+            sc = 0.5 * (ks @ q[b, h])
+            w_ = np.exp(sc - sc.max())
+            _close(got[b, h], (w_ / w_.sum()) @ vs, 1e-13, f"decode seq {b} head {h}")
+
+
+def pin_lse_merges_split_keys(orc):
+    """Two halves of a row's keys, each with its output and LSE, merge into the
+    whole row: o = (o1 e^lse1 + o2 e^lse2) / (e^lse1 + e^lse2), lse = log(e^lse1 + e^lse2)."""
+    n, a = 50, 21
+    q, k, v = _rand([0, n], 2, 1, 8, 33)
+    qr = q[n - 1:n]
+    whole, lw = orc.attention(qr, k, v, [0, 1], "full", 0.9, return_lse=True, cu_seqlens_k=[0, n])
+    o1, l1 = orc.attention(qr, k[:a], v[:a], [0, 1], "full", 0.9, return_lse=True, cu_seqlens_k=[0, a])
+    o2, l2 = orc.attention(qr, k[a:], v[a:], [0, 1], "full", 0.9, return_lse=True, cu_seqlens_k=[0, n - a])
+    mx = np.maximum(l1, l2)
+    w1, w2 = np.exp(l1 - mx), np.exp(l2 - mx)
+    merged = (o1 * w1[..., None] + o2 * w2[..., None]) / (w1 + w2)[..., None]
+    _close(merged, whole, 1e-13, "lse merge")
+    _close(mx + np.log(w1 + w2), lw, 1e-13, "lse merge lse")
+
+
+# ---------------------------------------------------------------------------
 # 5. exact integer probes (expected integers from the explicit visible sets)
 # ---------------------------------------------------------------------------
 
@@ -432,5 +538,7 @@ ALL_PINS = [
     pin_first_row_and_single_token, pin_constant_values, pin_wide_window_is_full,
     pin_two_key_sigmoid, pin_probabilities_sum_to_one, pin_key_shift, pin_joint_permutation,
     pin_gqa_equals_repeated_mha, pin_packed_equals_separate, pin_rows_api_matches_full,
-    pin_lse_definition, pin_dense_bruteforce, pin_probe_count, pin_probe_index, pin_needle,
+    pin_lse_definition, pin_dense_bruteforce, pin_kv_torch_sdpa, pin_kv_suffix_of_square,
+    pin_kv_decode_single_query, pin_lse_merges_split_keys, pin_probe_count, pin_probe_index,
+    pin_needle,
 ]

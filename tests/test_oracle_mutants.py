@@ -26,15 +26,18 @@ MUTANTS = {
     "scale dropped": ("scores[j - lo] = scale * dot;", "scores[j - lo] = dot;"),
     "exponent sign flipped": ("exp(scores[j - lo] - m)", "exp(m - scores[j - lo])"),
     "max not subtracted": ("exp(scores[j - lo] - m)", "exp(scores[j - lo])"),
-    "scores use V": ("const double *kj = k + ", "const double *kj = v + "),
-    "key sequence offset dropped": ("k + ((size_t)(s0 + j) * hkv + g) * d",
-                                    "k + ((size_t)(j) * hkv + g) * d"),
-    "value head ignored": ("v + ((size_t)(s0 + j) * hkv + g) * d",
-                           "v + ((size_t)(s0 + j) * hkv) * d"),
+    "scores use V": ("const double *kj = kseq + ", "const double *kj = vseq + "),
+    "key sequence offset dropped": ("k + (size_t)cu_k[b] * hkv * d;", "k;"),
+    "value head ignored": ("vseq + ((size_t)j * hkv + g) * d", "vseq + ((size_t)j * hkv) * d"),
     "query head ignored": ("q + ((size_t)t * hq + h) * d", "q + ((size_t)t * hq) * d"),
     "normalisation dropped": ("double p = scores[j - lo] / l;", "double p = scores[j - lo];"),
     "sequence lookup off by one": ("(int64_t)cu[b + 1] <= t", "(int64_t)cu[b + 1] < t"),
     "lse drops the max": ("*lse = m + log(l);", "*lse = log(l);"),
+    "queries aligned top-left": ("int64_t pos = (t - cu_q[b]) + (lk - lq);",
+                                 "int64_t pos = (t - cu_q[b]);"),
+    "key count from the query packing": ("int64_t lk = (int64_t)cu_k[b + 1] - cu_k[b];",
+                                         "int64_t lk = (int64_t)cu_q[b + 1] - cu_q[b];"),
+    "values from the query packing": ("v + (size_t)cu_k[b] * hkv * d;", "v + (size_t)cu_q[b] * hkv * d;"),
 }
 
 
