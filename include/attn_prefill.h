@@ -112,6 +112,60 @@ int attn_prefill_check(const void *q, const void *k, const void *v,
                        int32_t head_dim, int32_t dtype, int32_t mask_kind,
                        int32_t window, float scale);
 
+/*
+ * Queries against a longer key/value sequence: chunked prefill over a
+ * resident key/value cache, and decode (one query per sequence).  The
+ * paper's system keeps its KV cache resident on the GPU (gist.science
+ * technical summary, Metodologia) and decodes over it after prefill (same
+ * summary, Contribuciones Clave y Resultados: greedy decode rate); this
+ * entry point computes the same exact attention for a call that brings only
+ * the newest queries.
+ *
+ * Sequence b holds Lq_b = cu_seqlens_q[b+1] - cu_seqlens_q[b] queries and
+ * Lk_b = cu_seqlens_k[b+1] - cu_seqlens_k[b] >= Lq_b keys/values.  The
+ * queries are the LAST Lq_b positions of the sequence ("bottom-right"
+ * alignment): local query i sits at position p = i + Lk_b - Lq_b and sees
+ *   ATTN_CAUSAL   keys 0..p
+ *   ATTN_FULL     keys 0..Lk_b-1
+ *   ATTN_WINDOW   the block of `window` tokens holding p (blocks aligned to
+ *                 the sequence start; the last may be shorter).
+ * With cu_seqlens_q equal to cu_seqlens_k element by element this is
+ * attn_prefill.
+ *
+ *   q, out         [Tq][n_q_heads][head_dim], Tq = cu_seqlens_q[n_seqs]
+ *   k, v           [Tk][n_kv_heads][head_dim], Tk = cu_seqlens_k[n_seqs]
+ *   lse            NULL, or a device float32 [Tq][n_q_heads], 4-byte aligned
+ *                  and overlapping no other buffer, that receives for every
+ *                  row ln(sum_j exp(scale * <q, k_j>)) over its visible keys:
+ *                  with out, what merges the results of two calls over
+ *                  disjoint key ranges exactly,
+ *                  o = (o1 e^lse1 + o2 e^lse2) / (e^lse1 + e^lse2).
+ *                  Accurate to ~2^-8 absolute for bf16 inputs (the row sum is
+ *                  taken over bf16-rounded probabilities), ~1e-6 for fp32.
+ *   cu_seqlens_q   host int32[n_seqs + 1], cu_seqlens_q[0] = 0, non-decreasing
+ *   cu_seqlens_k   host int32[n_seqs + 1], cu_seqlens_k[0] = 0, non-decreasing
+ *   other arguments as for attn_prefill.
+ *
+ * Returns the codes of attn_prefill, plus ATTN_EINVAL when some Lq_b > Lk_b,
+ * lse is misaligned or overlaps q, k, v or out.  Tq = 0 succeeds without
+ * device work.  Ownership, execution and determinism as for attn_prefill.
+ */
+int attn_prefill_kv(const void *q, const void *k, const void *v, void *out, float *lse,
+                    const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                    int32_t n_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                    int32_t head_dim, int32_t dtype, int32_t mask_kind,
+                    int32_t window, float scale, void *stream);
+
+/* The argument checks of attn_prefill_kv alone (host-only, like
+ * attn_prefill_check). */
+int attn_prefill_kv_check(const void *q, const void *k, const void *v,
+                          const void *out, const float *lse,
+                          const int32_t *cu_seqlens_q,
+                          const int32_t *cu_seqlens_k, int32_t n_seqs,
+                          int32_t n_q_heads, int32_t n_kv_heads,
+                          int32_t head_dim, int32_t dtype, int32_t mask_kind,
+                          int32_t window, float scale);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *attn_strerror(int status);
 

@@ -5,7 +5,11 @@ include/attn_prefill.h); this module only marshals torch tensors to it.  The
 functions carry the C entry points' names:
 
 * ``attn_prefill(q, k, v, cu_seqlens, mask="causal", scale=None, out=None)``
-* ``attn_prefill_check(...)``, ``attn_strerror(status)``, ``attn_version()``
+* ``attn_prefill_kv(q, k, v, cu_seqlens_q, cu_seqlens_k, mask="causal",
+  scale=None, out=None, lse=False)`` -- queries that end a longer key
+  sequence (chunked prefill, decode), optionally with the log-sum-exp
+* ``attn_prefill_check(...)``, ``attn_prefill_kv_check(...)``,
+  ``attn_strerror(status)``, ``attn_version()``
 
 There is no fallback: if the library is missing or cannot be loaded, the
 call raises.
@@ -16,7 +20,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["attn_prefill", "attn_prefill_check", "attn_strerror", "attn_version",
+__all__ = ["attn_prefill", "attn_prefill_check", "attn_prefill_kv", "attn_prefill_kv_check",
+           "attn_strerror", "attn_version",
            "AttnError", "library_path", "load_library", "ATTN_OK", "ATTN_EINVAL",
            "ATTN_EUNSUPPORTED", "ATTN_ELAUNCH", "ATTN_BF16", "ATTN_F32", "ATTN_CAUSAL",
            "ATTN_FULL", "ATTN_WINDOW"]
@@ -60,6 +65,12 @@ def load_library() -> ctypes.CDLL:
     lib.attn_prefill_check.argtypes = [vp, vp, vp, vp, ip, i32, i32, i32, i32, i32, i32, i32,
                                        ctypes.c_float]
     lib.attn_prefill_check.restype = ctypes.c_int
+    lib.attn_prefill_kv.argtypes = [vp, vp, vp, vp, vp, ip, ip, i32, i32, i32, i32, i32, i32,
+                                    i32, ctypes.c_float, vp]
+    lib.attn_prefill_kv.restype = ctypes.c_int
+    lib.attn_prefill_kv_check.argtypes = [vp, vp, vp, vp, vp, ip, ip, i32, i32, i32, i32, i32,
+                                          i32, i32, ctypes.c_float]
+    lib.attn_prefill_kv_check.restype = ctypes.c_int
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -154,3 +165,74 @@ def attn_prefill_check(q, k, v, cu_seqlens, mask="causal", scale=None, out=None)
         out = torch.empty_like(q)
     a = _args(q, k, v, out, cu_seqlens, mask, scale)
     return int(load_library().attn_prefill_check(*a))
+
+
+def _args_kv(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, mask, scale):
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [Tq, Hq, d]; k and v [Tk, Hkv, d]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.shape != v.shape or k.shape[2] != q.shape[2]:
+        raise ValueError("q, k, v shapes disagree")
+    if out.shape != q.shape or out.dtype != q.dtype or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v and out must share dtype; out must have q's shape")
+    if lse is not None:
+        import torch
+
+        if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:2]) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [Tq, Hq] tensor")
+    kind, window = _mask_args(mask)
+    d = int(q.shape[2])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    cu_q, n_q = _cu_array(cu_seqlens_q)
+    cu_k, n_k = _cu_array(cu_seqlens_k)
+    if n_q != n_k:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if n_q >= 0 and (int(cu_q[n_q]) != q.shape[0] or int(cu_k[n_k]) != k.shape[0]):
+        raise ValueError("cu_seqlens_q[-1] must equal Tq and cu_seqlens_k[-1] must equal Tk")
+    return (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            None if lse is None else lse.data_ptr(), cu_q, cu_k, n_q, int(q.shape[1]),
+            int(k.shape[1]), d, _dtype_code(q), kind, window, float(scale))
+
+
+def attn_prefill_kv(q, k, v, cu_seqlens_q, cu_seqlens_k, mask="causal", scale=None, out=None,
+                    lse=False, stream=None):
+    """Exact attention of queries that end longer key sequences.
+
+    q: [Tq, Hq, d], k/v: [Tk, Hkv, d]; sequence b has its last
+    cu_seqlens_q[b+1]-cu_seqlens_q[b] positions as queries over
+    cu_seqlens_k[b+1]-cu_seqlens_k[b] keys.  ``lse``: False (not computed),
+    True (allocated and returned) or a float32 [Tq, Hq] tensor to fill.
+    Returns ``out``, or ``(out, lse)`` when lse is requested.
+    """
+    import torch
+
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    lse_t = None
+    if lse is True:
+        lse_t = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    elif lse is not False and lse is not None:
+        lse_t = lse
+    a = _args_kv(q, k, v, out, lse_t, cu_seqlens_q, cu_seqlens_k, mask, scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream or 0)
+    status = lib.attn_prefill_kv(*a, ctypes.c_void_p(handle))
+    if status != ATTN_OK:
+        raise AttnError(status, "attn_prefill_kv")
+    return out if lse_t is None else (out, lse_t)
+
+
+def attn_prefill_kv_check(q, k, v, cu_seqlens_q, cu_seqlens_k, mask="causal", scale=None,
+                          out=None, lse=None) -> int:
+    """Status attn_prefill_kv would return for these arguments (host-only)."""
+    import torch
+
+    if out is None:
+        out = torch.empty_like(q)
+    a = _args_kv(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, mask, scale)
+    return int(load_library().attn_prefill_kv_check(*a))

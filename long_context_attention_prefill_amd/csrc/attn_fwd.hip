@@ -17,13 +17,17 @@
 //
 // fp32 family: vector-ALU kernel, two lanes per query row, K/V tiles in LDS.
 //
-// Visible keys of local row i (sequence of n tokens) form one interval
+// A sequence holds nq queries and nk >= nq keys; its queries are the last nq
+// positions, so local query row r sits at position i = r + (nk - nq) (equal
+// counts: i = r).  Visible keys of position i form one interval
 // [lo(i), hi(i)) for all three masks, computed with integers only:
-//   causal [0, i+1)   full [0, n)   window [W*floor(i/W), min(W*floor(i/W)+W, n))
+//   causal [0, i+1)   full [0, nk)  window [W*floor(i/W), min(W*floor(i/W)+W, nk))
 // lo and hi never decrease with i, so a tile of rows sees the union
 // [lo(first), hi(last)) and every row sees the intersection
 // [lo(last), hi(first)); only key tiles not inside the intersection are
 // masked element by element, and tiles outside the union are never loaded.
+// With lse requested, each row also stores ln(sum_j exp(scale * s_j)) =
+// (m + log2(l)) * ln 2 from its exp2-unit reference m and sum l.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -42,6 +46,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.6931471805599453f;
 
 // Softmax runs in base 2 on scores pre-multiplied by scale*log2(e).  The
 // reference maximum is raised only when a row's new maximum exceeds it by
@@ -154,8 +159,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_generic(const LaunchArgs 
   const int g = lane >> 5;
 
   const Item it = decode_item(a, blockIdx.x);
-  const int s0 = a.seq_start[it.seq];
-  const int n = a.seq_len[it.seq];
+  const int s0q = a.q_start[it.seq], s0k = a.k_start[it.seq];
+  // queries are the last nq of nk positions: local row i sits at i + off
+  const int nq = a.q_len[it.seq], nk = a.k_len[it.seq], off = nk - nq;
   const int h = it.head;
   const int hk = h / a.group;
   const int mask = a.mask_kind;
@@ -165,23 +171,23 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_generic(const LaunchArgs 
   const float cabs = neg ? -c : c;
 
   const int q0 = it.tile * BM;
-  const int qend = min(q0 + BM, n);
+  const int qend = min(q0 + BM, nq);
   int kv_lo, kv_hi, tmp;
-  row_range(mask, W, q0, n, kv_lo, tmp);
-  row_range(mask, W, qend - 1, n, tmp, kv_hi);
+  row_range(mask, W, q0 + off, nk, kv_lo, tmp);
+  row_range(mask, W, qend - 1 + off, nk, tmp, kv_hi);
 
   const int wq0 = q0 + wave * 32;
-  const bool wave_active = wq0 < n;
+  const bool wave_active = wq0 < nq;
   int w_lo = 0, w_hi = 0, i_lo = 0, i_hi = 0;
   if (wave_active) {
-    const int wq1 = min(wq0 + 32, n);
-    row_range(mask, W, wq0, n, w_lo, i_hi);
-    row_range(mask, W, wq1 - 1, n, i_lo, w_hi);
+    const int wq1 = min(wq0 + 32, nq);
+    row_range(mask, W, wq0 + off, nk, w_lo, i_hi);
+    row_range(mask, W, wq1 - 1 + off, nk, i_lo, w_hi);
   }
   const int row = wq0 + l32;
-  const bool row_ok = row < n;
+  const bool row_ok = row < nq;
   int lo_r = 0, hi_r = 0;
-  if (row_ok) row_range(mask, W, row, n, lo_r, hi_r);
+  if (row_ok) row_range(mask, W, row + off, nk, lo_r, hi_r);
 
   // head-dim padding is read by the MFMAs and must hold zeros
   if constexpr (DK != D) {
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_generic(const LaunchArgs 
   bf16x8 qf[KSTEPS];
   {
     const __bf16 *qrow = reinterpret_cast<const __bf16 *>(a.q) +
-                         ((size_t)(s0 + (row_ok ? row : 0)) * a.hq + h) * D;
+                         ((size_t)(s0q + (row_ok ? row : 0)) * a.hq + h) * D;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       const int d0 = 16 * kk + 8 * g;
@@ -216,8 +222,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_generic(const LaunchArgs 
   }
 
   const size_t kv_rs = (size_t)a.hkv * D;  // elements between consecutive tokens
-  const __bf16 *kbase = reinterpret_cast<const __bf16 *>(a.k) + (size_t)s0 * kv_rs + (size_t)hk * D;
-  const __bf16 *vbase = reinterpret_cast<const __bf16 *>(a.v) + (size_t)s0 * kv_rs + (size_t)hk * D;
+  const __bf16 *kbase = reinterpret_cast<const __bf16 *>(a.k) + (size_t)s0k * kv_rs + (size_t)hk * D;
+  const __bf16 *vbase = reinterpret_cast<const __bf16 *>(a.v) + (size_t)s0k * kv_rs + (size_t)hk * D;
 
   u32x4 kreg[KLOADS];
   u32x4 vreg[VLOADS][4];
@@ -407,7 +413,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_generic(const LaunchArgs 
     const float l_tot = l_run + xor32(l_run);
     if (row_ok) {
       const float inv = 1.0f / l_tot;
-      __bf16 *orow = reinterpret_cast<__bf16 *>(a.out) + ((size_t)(s0 + row) * a.hq + h) * D;
+      if (a.lse != nullptr && g == 0)
+        a.lse[(size_t)(s0q + row) * a.hq + h] = (m_run + log2f(l_tot)) * kLn2;
+      __bf16 *orow = reinterpret_cast<__bf16 *>(a.out) + ((size_t)(s0q + row) * a.hq + h) * D;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -518,8 +526,9 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
   const int g = lane >> 5;
 
   const Item it = decode_item(a, blockIdx.x);
-  const int s0 = a.seq_start[it.seq];
-  const int n = a.seq_len[it.seq];
+  const int s0q = a.q_start[it.seq], s0k = a.k_start[it.seq];
+  // queries are the last nq of nk positions: local row i sits at i + off
+  const int nq = a.q_len[it.seq], nk = a.k_len[it.seq], off = nk - nq;
   const int h = it.head;
   const int hk = h / a.group;
   const int mask = a.mask_kind;
@@ -531,20 +540,20 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
   const float cabs = neg ? -c : c;
 
   const int q0 = it.tile * BM;
-  const int qend = min(q0 + BM, n);
+  const int qend = min(q0 + BM, nq);
   int kv_lo, kv_hi, tmp;
-  row_range(mask, W, q0, n, kv_lo, tmp);
-  row_range(mask, W, qend - 1, n, tmp, kv_hi);
+  row_range(mask, W, q0 + off, nk, kv_lo, tmp);
+  row_range(mask, W, qend - 1 + off, nk, tmp, kv_hi);
 
   // The wave's rows [wq0, wq0 + 32R): the union of their visible keys is
   // [w_lo, w_hi), the intersection [i_lo, i_hi).
   const int wq0 = q0 + wave * 32 * R;
-  const bool wave_active = wq0 < n;
+  const bool wave_active = wq0 < nq;
   int w_lo = 0, w_hi = 0, i_lo = 0, i_hi = 0;
   if (wave_active) {
-    const int wq1 = min(wq0 + 32 * R, n);
-    row_range(mask, W, wq0, n, w_lo, i_hi);
-    row_range(mask, W, wq1 - 1, n, i_lo, w_hi);
+    const int wq1 = min(wq0 + 32 * R, nq);
+    row_range(mask, W, wq0 + off, nk, w_lo, i_hi);
+    row_range(mask, W, wq1 - 1 + off, nk, i_lo, w_hi);
   }
   // Sub-block r: this lane's query row wq0 + 32r + l32.
   int row[R], lo_r[R], hi_r[R];
@@ -552,10 +561,10 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     row[r] = wq0 + 32 * r + l32;
-    row_ok[r] = row[r] < n;
+    row_ok[r] = row[r] < nq;
     lo_r[r] = 0;
     hi_r[r] = 0;
-    if (row_ok[r]) row_range(mask, W, row[r], n, lo_r[r], hi_r[r]);
+    if (row_ok[r]) row_range(mask, W, row[r] + off, nk, lo_r[r], hi_r[r]);
   }
 
   // Q fragments (B operand of S^T = K Q^T): lane (l32, g) of sub-block r
@@ -564,7 +573,7 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const __bf16 *qrow = reinterpret_cast<const __bf16 *>(a.q) +
-                         ((size_t)(s0 + (row_ok[r] ? row[r] : 0)) * a.hq + h) * D;
+                         ((size_t)(s0q + (row_ok[r] ? row[r] : 0)) * a.hq + h) * D;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk)
       qf[r][kk] = row_ok[r] ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * kk + 8 * g)
@@ -581,8 +590,8 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
     const int rr = p / L::SLOTS, cs = p % L::SLOTS;
     ld_off[i] = cs < CH ? (uint32_t)(rr * rowbytes + cs * 16) : kOutOfRange;
   }
-  const char *kseq = reinterpret_cast<const char *>(a.k) + ((size_t)s0 * a.hkv + hk) * D * 2;
-  const char *vseq = reinterpret_cast<const char *>(a.v) + ((size_t)s0 * a.hkv + hk) * D * 2;
+  const char *kseq = reinterpret_cast<const char *>(a.k) + ((size_t)s0k * a.hkv + hk) * D * 2;
+  const char *vseq = reinterpret_cast<const char *>(a.v) + ((size_t)s0k * a.hkv + hk) * D * 2;
 
   // Direct loads of the K (or V) rows kt .. kt+63 into an LDS buffer.
   // kt >= kv_hi is allowed: the range is then empty, nothing is fetched and
@@ -773,8 +782,8 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
   int t_plain0 = 1, t_plain1 = 1;
   {
     int wlo, whi, tmp2;
-    row_range(mask, W, qend - 1, n, wlo, tmp2);
-    row_range(mask, W, q0, n, tmp2, whi);
+    row_range(mask, W, qend - 1 + off, nk, wlo, tmp2);
+    row_range(mask, W, q0 + off, nk, tmp2, whi);
     const int first = max(1, (wlo - kv_lo + BN - 1) / BN);
     const int last = max(0, (whi - kv_lo) / BN);  // tiles [0, last) end at or before whi
     if (last > first) {
@@ -934,7 +943,9 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
       const float l_tot = l_run[r] + xor32(l_run[r]);
       if (row_ok[r]) {
         const float inv = 1.0f / l_tot;
-        __bf16 *orow = reinterpret_cast<__bf16 *>(a.out) + ((size_t)(s0 + row[r]) * a.hq + h) * D;
+        if (a.lse != nullptr && g == 0)
+          a.lse[(size_t)(s0q + row[r]) * a.hq + h] = (m_ref[r] + log2f(l_tot)) * kLn2;
+        __bf16 *orow = reinterpret_cast<__bf16 *>(a.out) + ((size_t)(s0q + row[r]) * a.hq + h) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -972,8 +983,9 @@ __global__ __launch_bounds__(256) void fwd_f32(const LaunchArgs a) {
   const int tid = threadIdx.x;
   const int half = tid & 1;
   const Item it = decode_item(a, blockIdx.x);
-  const int s0 = a.seq_start[it.seq];
-  const int n = a.seq_len[it.seq];
+  const int s0q = a.q_start[it.seq], s0k = a.k_start[it.seq];
+  // queries are the last nq of nk positions: local row i sits at i + off
+  const int nq = a.q_len[it.seq], nk = a.k_len[it.seq], off = nk - nq;
   const int h = it.head;
   const int hk = h / a.group;
   const int mask = a.mask_kind;
@@ -981,20 +993,20 @@ __global__ __launch_bounds__(256) void fwd_f32(const LaunchArgs a) {
   const float c = a.c;
 
   const int q0 = it.tile * BM;
-  const int qend = min(q0 + BM, n);
+  const int qend = min(q0 + BM, nq);
   int kv_lo, kv_hi, tmp;
-  row_range(mask, W, q0, n, kv_lo, tmp);
-  row_range(mask, W, qend - 1, n, tmp, kv_hi);
+  row_range(mask, W, q0 + off, nk, kv_lo, tmp);
+  row_range(mask, W, qend - 1 + off, nk, tmp, kv_hi);
 
   const int row = q0 + (tid >> 1);
-  const bool row_ok = row < n;
+  const bool row_ok = row < nq;
   int lo_r = 0, hi_r = 0;
-  if (row_ok) row_range(mask, W, row, n, lo_r, hi_r);
+  if (row_ok) row_range(mask, W, row + off, nk, lo_r, hi_r);
 
   float qv[DH], o[DH];
   {
     const float *qrow = reinterpret_cast<const float *>(a.q) +
-                        ((size_t)(s0 + (row_ok ? row : 0)) * a.hq + h) * D + half * DH;
+                        ((size_t)(s0q + (row_ok ? row : 0)) * a.hq + h) * D + half * DH;
 #pragma unroll
     for (int e = 0; e < DH; e += 4) {
       f32x4 x = row_ok ? *reinterpret_cast<const f32x4 *>(qrow + e) : (f32x4)(0.0f);
@@ -1009,8 +1021,8 @@ __global__ __launch_bounds__(256) void fwd_f32(const LaunchArgs a) {
   float m_run = kNegInf, l_run = 0.0f;
 
   const size_t kv_rs = (size_t)a.hkv * D;
-  const float *kbase = reinterpret_cast<const float *>(a.k) + (size_t)s0 * kv_rs + (size_t)hk * D;
-  const float *vbase = reinterpret_cast<const float *>(a.v) + (size_t)s0 * kv_rs + (size_t)hk * D;
+  const float *kbase = reinterpret_cast<const float *>(a.k) + (size_t)s0k * kv_rs + (size_t)hk * D;
+  const float *vbase = reinterpret_cast<const float *>(a.v) + (size_t)s0k * kv_rs + (size_t)hk * D;
 
   for (int kt = kv_lo; kt < kv_hi; kt += BN) {
     __syncthreads();  // previous tile fully consumed
@@ -1072,7 +1084,9 @@ __global__ __launch_bounds__(256) void fwd_f32(const LaunchArgs a) {
 
   if (row_ok) {
     const float inv = 1.0f / l_run;
-    float *orow = reinterpret_cast<float *>(a.out) + ((size_t)(s0 + row) * a.hq + h) * D + half * DH;
+    if (a.lse != nullptr && half == 0)
+      a.lse[(size_t)(s0q + row) * a.hq + h] = (m_run + log2f(l_run)) * kLn2;
+    float *orow = reinterpret_cast<float *>(a.out) + ((size_t)(s0q + row) * a.hq + h) * D + half * DH;
 #pragma unroll
     for (int e = 0; e < DH; e += 4) {
       f32x4 w;

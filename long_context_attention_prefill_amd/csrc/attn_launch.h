@@ -15,13 +15,17 @@ constexpr int kMaxSeqsPerLaunch = 64;
 
 enum MaskKind : int32_t { kCausal = 0, kFull = 1, kWindow = 2 };
 
-// One launch: a group of non-empty sequences sorted by length, longest
-// first, and everything a workgroup needs to find its item.
+// One launch: a group of sequences with at least one query, sorted by query
+// count, most first, and everything a workgroup needs to find its item.
+// Sequence i has q_len[i] queries and k_len[i] >= q_len[i] keys; its queries
+// are the last q_len[i] positions, so local query r sits at position
+// r + k_len[i] - q_len[i].
 struct LaunchArgs {
   const void *q;
   const void *k;
   const void *v;
   void *out;
+  float *lse;          // [Tq][hq] natural-log sum of exp(scale * score), or null
   int32_t hq;          // query heads
   int32_t hkv;         // key/value heads
   int32_t group;       // hq / hkv
@@ -31,9 +35,11 @@ struct LaunchArgs {
   int32_t n_seqs;      // sequences in this launch (<= kMaxSeqsPerLaunch)
   int32_t bm;          // query rows per workgroup
   int32_t total_items; // workgroups = hq * sum(seq_tiles)
-  int32_t seq_start[kMaxSeqsPerLaunch];  // packed index of token 0
-  int32_t seq_len[kMaxSeqsPerLaunch];    // tokens
-  int32_t seq_tiles[kMaxSeqsPerLaunch];  // ceil(len / bm), non-increasing
+  int32_t q_start[kMaxSeqsPerLaunch];    // packed index of the first query
+  int32_t q_len[kMaxSeqsPerLaunch];      // queries
+  int32_t k_start[kMaxSeqsPerLaunch];    // packed index of the first key/value
+  int32_t k_len[kMaxSeqsPerLaunch];      // keys/values, >= q_len
+  int32_t seq_tiles[kMaxSeqsPerLaunch];  // ceil(q_len / bm), non-increasing
   // Causal order only (items by query-tile level, heaviest first): query-tile
   // levels m in [seq_tiles[k], seq_tiles[k-1]) hold the k longest sequences,
   // and their items start at level_start[k-1]; level_start[n_seqs] =

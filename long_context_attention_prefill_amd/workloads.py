@@ -173,11 +173,13 @@ def random_case(seed, max_seqs=4, max_len=300, dims=(64, 72, 128), ratios=(1, 2,
 CHUNK = 16  # keys per class in the count probe
 
 
-def probe_count_inputs(cu, hq, hkv, d):
+def probe_count_inputs(cu, hq, hkv, d, cu_k=None):
     """Q = 0 (every visible key weighs the same); V[j, g, c] = 1 iff c is the
-    class of packed key j, class = (j // 16) mod d."""
-    T = int(cu[-1])
-    q = np.zeros((T, hq, d))
+    class of packed key j, class = (j // 16) mod d.  cu_k: the keys' own
+    packing when it differs from the queries' (cu)."""
+    Tq = int(cu[-1])
+    T = int((cu if cu_k is None else cu_k)[-1])
+    q = np.zeros((Tq, hq, d))
     k = np.zeros((T, hkv, d))
     v = np.zeros((T, hkv, d))
     j = np.arange(T)
@@ -185,15 +187,16 @@ def probe_count_inputs(cu, hq, hkv, d):
     return q, k, v
 
 
-def probe_index_inputs(cu, hq, hkv, d, sign):
+def probe_index_inputs(cu, hq, hkv, d, sign, cu_k=None):
     """K[j] = (j >> 7, j & 127, 0, ...) from the packed index j; Q = sign *
     (2^17, 2^9, 0, ...).  The logit is then strictly monotone in j with gaps of
     at least 512 * scale, so the weight sits on the last (sign=+1) or first
     (sign=-1) visible key.  V[j, g, b] = bit b of j for b < 15, and
-    V[j, g, 15 + g] = 1 marks the KV head."""
-    T = int(cu[-1])
+    V[j, g, 15 + g] = 1 marks the KV head.  cu_k: the keys' own packing."""
+    Tq = int(cu[-1])
+    T = int((cu if cu_k is None else cu_k)[-1])
     assert d >= 16 + hkv and T < (1 << 15)
-    q = np.zeros((T, hq, d))
+    q = np.zeros((Tq, hq, d))
     k = np.zeros((T, hkv, d))
     v = np.zeros((T, hkv, d))
     j = np.arange(T)

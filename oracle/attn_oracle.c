@@ -39,9 +39,10 @@
  * tokens cu_seqlens[b] .. cu_seqlens[b+1]-1.
  *
  * Queries against a longer key sequence (the *_kv entry points).  The
- * document pages keep the key/value cache resident on the GPU and run
- * prefill and then decode over it (gist.science technical summary, KV cache
- * and decode figures), so a call may hold fewer new queries than keys:
+ * paper's system keeps its key/value cache resident on the GPU (gist.science
+ * technical summary, Metodologia) and decodes over it after prefill (same
+ * summary, Contribuciones Clave y Resultados), so a call may hold fewer new
+ * queries than keys:
  * q[Tq][Hq][d] packed by cu_q, k/v[Tk][Hkv][d] packed by cu_k, with
  * Lq_b = cu_q[b+1]-cu_q[b] <= Lk_b = cu_k[b+1]-cu_k[b].  The pages do not say
  * where those queries sit; the plain reading is that they are the LAST Lq_b

@@ -40,3 +40,25 @@ def max_err(a, b):
         return 0.0
     assert np.all(np.isfinite(a)), "non-finite GPU output"
     return float(np.max(np.abs(a - b)))
+
+
+# log-sum-exp tolerance: the bf16 path sums bf16-rounded probabilities (each
+# within 2^-9 relative), so ln(sum) is within 2^-9 of exact; 2^-8 leaves a
+# factor 2 for the fp32 score and exp2 rounding.  The fp32 path sums fp32
+# probabilities: within n * 2^-24 relative, < 1e-4 for the sizes tested.
+LSE_TOL = {"bf16": 2.0 ** -8, "f32": 1e-4}
+
+
+def run_hip_kv(q, k, v, cu_q, cu_k, mask, scale, dtype, lse=True):
+    import torch
+
+    import long_context_attention_prefill_amd as lcap
+
+    tq, tk, tv = to_device(q, dtype), to_device(k, dtype), to_device(v, dtype)
+    res = lcap.attn_prefill_kv(tq, tk, tv, [int(x) for x in cu_q], [int(x) for x in cu_k],
+                               mask=mask, scale=scale, lse=lse)
+    torch.cuda.synchronize()
+    if lse:
+        out, l = res
+        return out.double().cpu().numpy(), l.double().cpu().numpy()
+    return res.double().cpu().numpy()

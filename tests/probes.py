@@ -71,3 +71,54 @@ def check_index_output(out, cu, mask, hq, hkv, sign):
     want_marks = np.zeros((hq, hkv), dtype=np.int64)
     want_marks[np.arange(hq), np.arange(hq) // (hq // hkv)] = 1
     assert np.array_equal(marks, np.broadcast_to(want_marks, marks.shape)), "kv head marker"
+
+
+# ---------------------------------------------------------------- queries ending longer key sequences
+
+def visible_interval_kv(cu_q, cu_k, mask):
+    """Packed key [lo, hi) for every packed query row when the Lq queries of a
+    sequence are the last Lq of its Lk positions (query i at i + Lk - Lq)."""
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_k = np.asarray(cu_k, dtype=np.int64)
+    Tq = int(cu_q[-1])
+    lo = np.zeros(Tq, dtype=np.int64)
+    hi = np.zeros(Tq, dtype=np.int64)
+    for b in range(len(cu_q) - 1):
+        sq, eq = int(cu_q[b]), int(cu_q[b + 1])
+        sk, nk = int(cu_k[b]), int(cu_k[b + 1] - cu_k[b])
+        pos = np.arange(eq - sq) + (nk - (eq - sq))
+        if mask == "causal":
+            lo[sq:eq], hi[sq:eq] = sk, sk + pos + 1
+        elif mask == "full":
+            lo[sq:eq], hi[sq:eq] = sk, sk + nk
+        else:
+            w = int(mask[1])
+            start = (pos // w) * w
+            lo[sq:eq] = sk + start
+            hi[sq:eq] = sk + np.minimum(start + w, nk)
+    return lo, hi
+
+
+def check_count_output_kv(out, cu_q, cu_k, mask, d):
+    Tk = int(cu_k[-1])
+    cls = (np.arange(Tk) // W.CHUNK) % d
+    pref = np.zeros((Tk + 1, d), dtype=np.int64)
+    np.add.at(pref, (np.arange(Tk) + 1, cls), 1)
+    pref = np.cumsum(pref, axis=0)
+    lo, hi = visible_interval_kv(cu_q, cu_k, mask)
+    want, nvis = pref[hi] - pref[lo], hi - lo
+    got = np.rint(np.asarray(out, dtype=np.float64) * nvis[:, None, None]).astype(np.int64)
+    bad = np.argwhere(got != want[:, None, :])
+    assert bad.size == 0, f"count probe mismatch at (t, h, class) {bad[:5].tolist()}"
+
+
+def check_index_output_kv(out, cu_q, cu_k, mask, hq, hkv, sign):
+    lo, hi = visible_interval_kv(cu_q, cu_k, mask)
+    want = (hi - 1) if sign > 0 else lo
+    got = decode_indices(out)
+    bad = np.argwhere(got != want[:, None])
+    assert bad.size == 0, f"index probe mismatch at (t, h) {bad[:5].tolist()}"
+    marks = np.rint(np.asarray(out[..., 15:15 + hkv], dtype=np.float64)).astype(np.int64)
+    want_marks = np.zeros((hq, hkv), dtype=np.int64)
+    want_marks[np.arange(hq), np.arange(hq) // (hq // hkv)] = 1
+    assert np.array_equal(marks, np.broadcast_to(want_marks, marks.shape)), "kv head marker"

@@ -101,3 +101,51 @@ def test_prefill_rejects_before_any_device_work(lib):
     # T = 0 succeeds with no work
     z = (ctypes.c_int32 * 3)(0, 0, 0)
     assert lib.attn_prefill(0, 0, 0, 0, z, 2, 4, 2, 128, 1, 0, 0, ctypes.c_float(0.1), None) == 0
+
+
+# ---------------------------------------------------------------- attn_prefill_kv
+
+L = 0x50000000  # fake, aligned lse address
+
+
+def check_kv(lib, q=Q, k=K, v=V, o=O, lse=L, cu_q=(0, 4, 5), cu_k=(0, 10, 30), hq=4, hkv=2,
+             d=128, dtype=1, mask=0, window=0, scale=0.1, n_seqs=None):
+    aq = (ctypes.c_int32 * len(cu_q))(*cu_q)
+    ak = (ctypes.c_int32 * len(cu_k))(*cu_k)
+    if n_seqs is None:
+        n_seqs = len(cu_q) - 1
+    return lib.attn_prefill_kv_check(q, k, v, o, lse, aq, ak, n_seqs, hq, hkv, d, dtype, mask,
+                                     window, ctypes.c_float(scale))
+
+
+def test_kv_check_accepts_valid(lib):
+    assert check_kv(lib) == lcap.ATTN_OK
+    assert check_kv(lib, lse=None) == lcap.ATTN_OK
+    assert check_kv(lib, cu_q=(0, 10, 30), cu_k=(0, 10, 30)) == lcap.ATTN_OK  # square
+    assert check_kv(lib, cu_q=(0, 1, 2), cu_k=(0, 100, 101)) == lcap.ATTN_OK  # decode
+    for mask, w in ((0, 0), (1, 0), (2, 7)):
+        assert check_kv(lib, mask=mask, window=w) == lcap.ATTN_OK
+    # no queries at all: nothing to launch, no pointer needed
+    assert check_kv(lib, q=0, o=0, lse=0, cu_q=(0, 0, 0)) == lcap.ATTN_OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(cu_q=(0, 11, 12)),                  # more queries than keys in sequence 0
+    dict(cu_q=(0, 4, 25)),                   # more queries than keys in sequence 1
+    dict(cu_k=(1, 10, 30)), dict(cu_q=(1, 4, 5)),
+    dict(cu_k=(0, 10, 5)), dict(cu_q=(0, 4, 3)),
+    dict(lse=L + 2), dict(lse=Q), dict(lse=O + 64), dict(lse=K + 4096),
+    dict(o=K), dict(q=0), dict(k=K + 8),
+], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_kv_check_rejects_invalid(lib, kw):
+    assert check_kv(lib, **kw) == lcap.ATTN_EINVAL
+
+
+def test_kv_rejects_before_any_device_work(lib):
+    aq = (ctypes.c_int32 * 2)(0, 9)
+    ak = (ctypes.c_int32 * 2)(0, 8)
+    st = lib.attn_prefill_kv(Q, K, V, O, L, aq, ak, 1, 4, 2, 128, 1, 0, 0, ctypes.c_float(0.1), None)
+    assert st == lcap.ATTN_EINVAL
+    z = (ctypes.c_int32 * 2)(0, 0)
+    assert lib.attn_prefill_kv(0, K, V, 0, 0, z, ak, 1, 4, 2, 128, 1, 0, 0, ctypes.c_float(0.1),
+                               None) == 0
