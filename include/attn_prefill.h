@@ -166,6 +166,48 @@ int attn_prefill_kv_check(const void *q, const void *k, const void *v,
                           int32_t head_dim, int32_t dtype, int32_t mask_kind,
                           int32_t window, float scale);
 
+/*
+ * Decode: the attention of each sequence's newest token over its whole
+ * key/value cache -- one query per sequence, the step the paper's system
+ * repeats per generated token over its GPU-resident cache (gist.science
+ * technical summary, Metodologia; Contribuciones Clave y Resultados: greedy
+ * decode rate).  The result is attn_prefill_kv with cu_seqlens_q = 0, 1, ...,
+ * n_seqs; for bf16 with head_dim 64 or 128 the visible keys of each sequence
+ * are cut into chunks computed in parallel and merged exactly through their
+ * references and sums, which needs a workspace.
+ *
+ *   q, out         [n_seqs][n_q_heads][head_dim]: row b is sequence b's query
+ *   k, v           [Tk][n_kv_heads][head_dim], Tk = cu_seqlens_k[n_seqs]
+ *   lse            NULL or device float32 [n_seqs][n_q_heads], as for
+ *                  attn_prefill_kv
+ *   cu_seqlens_k   host int32[n_seqs + 1], cu_seqlens_k[0] = 0, strictly
+ *                  increasing (every sequence holds at least one key)
+ *   workspace      device scratch of workspace_bytes >= the size
+ *                  attn_decode_workspace_size reports for the same shape,
+ *                  16-byte aligned, overlapping no other buffer; may be NULL
+ *                  when that size is 0.  The caller owns it; calls that share
+ *                  one workspace must be ordered (same stream).
+ *   other arguments as for attn_prefill.
+ *
+ * Returns the codes of attn_prefill_kv, plus ATTN_EINVAL for an empty
+ * sequence or a missing, small, misaligned or overlapping workspace.
+ * n_seqs = 0 succeeds without device work.
+ */
+int attn_decode(const void *q, const void *k, const void *v, void *out, float *lse,
+                const int32_t *cu_seqlens_k, int32_t n_seqs, int32_t n_q_heads,
+                int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                int32_t mask_kind, int32_t window, float scale, void *workspace,
+                uint64_t workspace_bytes, void *stream);
+
+/* Bytes of workspace attn_decode needs for this shape (0 when it splits no
+ * sequence's keys, or for dtypes and head dims it computes without
+ * splitting); host-only.  Returns the argument codes of attn_decode. */
+int attn_decode_workspace_size(const int32_t *cu_seqlens_k, int32_t n_seqs,
+                               int32_t n_q_heads, int32_t n_kv_heads,
+                               int32_t head_dim, int32_t dtype,
+                               int32_t mask_kind, int32_t window,
+                               uint64_t *bytes);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *attn_strerror(int status);
 

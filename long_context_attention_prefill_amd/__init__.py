@@ -8,8 +8,11 @@ functions carry the C entry points' names:
 * ``attn_prefill_kv(q, k, v, cu_seqlens_q, cu_seqlens_k, mask="causal",
   scale=None, out=None, lse=False)`` -- queries that end a longer key
   sequence (chunked prefill, decode), optionally with the log-sum-exp
+* ``attn_decode(q, k, v, cu_seqlens_k, mask="causal", scale=None, out=None,
+  lse=False, workspace=None)`` -- one query per sequence over its cache
 * ``attn_prefill_check(...)``, ``attn_prefill_kv_check(...)``,
-  ``attn_strerror(status)``, ``attn_version()``
+  ``attn_decode_workspace_size(...)``, ``attn_strerror(status)``,
+  ``attn_version()``
 
 There is no fallback: if the library is missing or cannot be loaded, the
 call raises.
@@ -21,7 +24,7 @@ import math
 import os
 
 __all__ = ["attn_prefill", "attn_prefill_check", "attn_prefill_kv", "attn_prefill_kv_check",
-           "attn_strerror", "attn_version",
+           "attn_decode", "attn_decode_workspace_size", "attn_strerror", "attn_version",
            "AttnError", "library_path", "load_library", "ATTN_OK", "ATTN_EINVAL",
            "ATTN_EUNSUPPORTED", "ATTN_ELAUNCH", "ATTN_BF16", "ATTN_F32", "ATTN_CAUSAL",
            "ATTN_FULL", "ATTN_WINDOW"]
@@ -71,6 +74,12 @@ def load_library() -> ctypes.CDLL:
     lib.attn_prefill_kv_check.argtypes = [vp, vp, vp, vp, vp, ip, ip, i32, i32, i32, i32, i32,
                                           i32, i32, ctypes.c_float]
     lib.attn_prefill_kv_check.restype = ctypes.c_int
+    lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, ip, i32, i32, i32, i32, i32, i32, i32,
+                                ctypes.c_float, vp, ctypes.c_uint64, vp]
+    lib.attn_decode.restype = ctypes.c_int
+    lib.attn_decode_workspace_size.argtypes = [ip, i32, i32, i32, i32, i32, i32, i32,
+                                               ctypes.POINTER(ctypes.c_uint64)]
+    lib.attn_decode_workspace_size.restype = ctypes.c_int
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -236,3 +245,55 @@ def attn_prefill_kv_check(q, k, v, cu_seqlens_q, cu_seqlens_k, mask="causal", sc
         out = torch.empty_like(q)
     a = _args_kv(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, mask, scale)
     return int(load_library().attn_prefill_kv_check(*a))
+
+
+def attn_decode_workspace_size(cu_seqlens_k, n_q_heads, n_kv_heads, head_dim, dtype=ATTN_BF16,
+                               mask="causal") -> int:
+    """Workspace bytes attn_decode needs for this shape (host-only)."""
+    kind, window = _mask_args(mask)
+    cu, n = _cu_array(cu_seqlens_k)
+    out = ctypes.c_uint64(0)
+    status = load_library().attn_decode_workspace_size(cu, n, int(n_q_heads), int(n_kv_heads),
+                                                       int(head_dim), int(dtype), kind, window,
+                                                       ctypes.byref(out))
+    if status != ATTN_OK:
+        raise AttnError(status, "attn_decode_workspace_size")
+    return int(out.value)
+
+
+def attn_decode(q, k, v, cu_seqlens_k, mask="causal", scale=None, out=None, lse=False,
+                workspace=None, stream=None):
+    """Attention of each sequence's newest token (row b of q) over its cache.
+
+    q: [n_seqs, Hq, d]; k/v: [Tk, Hkv, d] packed by cu_seqlens_k (host ints,
+    every sequence non-empty).  ``workspace``: a device tensor of at least
+    attn_decode_workspace_size(...) bytes, or None to allocate one here.
+    ``lse`` as for attn_prefill_kv.  Returns ``out`` or ``(out, lse)``.
+    """
+    import torch
+
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    lse_t = None
+    if lse is True:
+        lse_t = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    elif lse is not False and lse is not None:
+        lse_t = lse
+    n = q.shape[0]
+    cu_q = list(range(n + 1))
+    a = _args_kv(q, k, v, out, lse_t, cu_q, cu_seqlens_k, mask, scale)
+    qp, kp, vp_, op, lp, _, cu_k, n_seqs, hq, hkv, d, dt, kind, window, sc = a
+    need = attn_decode_workspace_size(cu_seqlens_k, hq, hkv, d, dt, mask)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream or 0)
+    status = lib.attn_decode(qp, kp, vp_, op, lp, cu_k, n_seqs, hq, hkv, d, dt, kind, window, sc,
+                             ws_ptr, ws_bytes, ctypes.c_void_p(handle))
+    if status != ATTN_OK:
+        raise AttnError(status, "attn_decode")
+    return out if lse_t is None else (out, lse_t)

@@ -24,12 +24,12 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Checks of every entry point.  cu_q / cu_k: host int32[n_seqs + 1]; with
-// cu_k == cu_q (the square case) every sequence has as many keys as queries.
-int check(const void *q, const void *k, const void *v, const void *out, const float *lse,
-          const int32_t *cu_q, const int32_t *cu_k, int32_t n_seqs, int32_t hq, int32_t hkv,
-          int32_t d, int32_t dtype, int32_t mask, int32_t window, float scale, int64_t *Tq_out,
-          int64_t *Tk_out) {
+// Checks of every entry point that involve no pointer.  cu_q / cu_k: host
+// int32[n_seqs + 1]; with cu_k == cu_q (the square case) every sequence has as
+// many keys as queries.
+int check_shape(const int32_t *cu_q, const int32_t *cu_k, int32_t n_seqs, int32_t hq, int32_t hkv,
+                int32_t d, int32_t dtype, int32_t mask, int32_t window, float scale,
+                int64_t *Tq_out, int64_t *Tk_out) {
   if (n_seqs < 0) return ATTN_EINVAL;
   if (n_seqs > 0 && (cu_q == nullptr || cu_k == nullptr)) return ATTN_EINVAL;
   if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return ATTN_EINVAL;
@@ -53,6 +53,19 @@ int check(const void *q, const void *k, const void *v, const void *out, const fl
   // element offsets: T * h * d must fit comfortably in 63 bits
   if (static_cast<double>(Tq) * hq * d > 9.0e18 || static_cast<double>(Tk) * hkv * d > 9.0e18)
     return ATTN_EUNSUPPORTED;
+  *Tq_out = Tq;
+  *Tk_out = Tk;
+  return ATTN_OK;
+}
+
+// Every check of an entry point: the shape, then the buffers.
+int check(const void *q, const void *k, const void *v, const void *out, const float *lse,
+          const int32_t *cu_q, const int32_t *cu_k, int32_t n_seqs, int32_t hq, int32_t hkv,
+          int32_t d, int32_t dtype, int32_t mask, int32_t window, float scale, int64_t *Tq_out,
+          int64_t *Tk_out) {
+  int64_t Tq = 0, Tk = 0;
+  const int rc = check_shape(cu_q, cu_k, n_seqs, hq, hkv, d, dtype, mask, window, scale, &Tq, &Tk);
+  if (rc != ATTN_OK) return rc;
   if (Tq > 0) {
     if (!q || !k || !v || !out) return ATTN_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_EINVAL;
@@ -141,6 +154,83 @@ int run(const void *q, const void *k, const void *v, void *out, float *lse,
   return ATTN_OK;
 }
 
+// ---------------------------------------------------------------- decode
+
+// The bf16 decode kernels cover head_dim 64 and 128; other requests run
+// through the prefill path as one query per sequence.
+bool decode_fast(int32_t dtype, int32_t d) { return dtype == ATTN_BF16 && (d == 64 || d == 128); }
+
+// Workers to aim for: 256 CUs x 4 waves, twice over, so chunks stay short
+// enough to spread a small batch over the whole GPU.
+constexpr int64_t kDecodeTargetItems = 2048;
+
+struct DecodePlan {
+  int32_t chunk = attn::kDecodeTile;
+  int64_t total_items = 0;
+  bool direct = true;
+  int32_t rows = 0, head_blocks = 0;
+};
+
+// Visible keys of the newest token of a sequence of n keys: [lo, n).
+int64_t decode_lo(int32_t mask, int32_t window, int64_t n) {
+  return mask == ATTN_WINDOW ? ((n - 1) / window) * window : 0;
+}
+
+DecodePlan plan_decode(const int32_t *cu_k, int32_t n_seqs, int32_t hq, int32_t hkv,
+                       int32_t mask, int32_t window) {
+  DecodePlan p;
+  const int32_t group = hq / hkv;
+  p.head_blocks = (group + 31) / 32;
+  p.rows = group < 32 ? group : 32;
+  int64_t tiles = 0;
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int64_t n = cu_k[b + 1] - cu_k[b];
+    const int64_t vis = n - decode_lo(mask, window, n);
+    tiles += (vis + attn::kDecodeTile - 1) / attn::kDecodeTile;
+  }
+  tiles *= static_cast<int64_t>(hkv) * p.head_blocks;
+  const int64_t per = (tiles + kDecodeTargetItems - 1) / kDecodeTargetItems;
+  p.chunk = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(per, 1 << 20)) * attn::kDecodeTile);
+  for (int32_t b = 0; b < n_seqs; ++b) {
+    const int64_t n = cu_k[b + 1] - cu_k[b];
+    const int64_t vis = n - decode_lo(mask, window, n);
+    const int64_t splits = (vis + p.chunk - 1) / p.chunk;
+    if (splits > 1) p.direct = false;
+    p.total_items += splits * hkv * p.head_blocks;
+  }
+  return p;
+}
+
+uint64_t decode_workspace_bytes(const DecodePlan &p, int32_t d) {
+  if (p.direct) return 0;
+  return static_cast<uint64_t>(p.total_items) * p.rows * (static_cast<uint64_t>(d) + 2) * sizeof(float);
+}
+
+// Decode takes one query (the newest token) per sequence, so every sequence
+// must hold at least one key; cu_q receives the queries' packing 0, 1, ..., n.
+int check_decode_shape(const int32_t *cu_k, int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d,
+                       int32_t dtype, int32_t mask, int32_t window, float scale,
+                       std::vector<int32_t> *cu_q) {
+  if (n_seqs < 0 || (n_seqs > 0 && cu_k == nullptr)) return ATTN_EINVAL;
+  for (int32_t b = 0; b < n_seqs; ++b)
+    if (cu_k[b + 1] <= cu_k[b]) return ATTN_EINVAL;  // an empty cache has no newest token
+  cu_q->resize(static_cast<size_t>(n_seqs) + 1);
+  for (int32_t b = 0; b <= n_seqs; ++b) (*cu_q)[b] = b;
+  int64_t Tq = 0, Tk = 0;
+  return check_shape(cu_q->data(), cu_k, n_seqs, hq, hkv, d, dtype, mask, window, scale, &Tq, &Tk);
+}
+
+int check_decode(const void *q, const void *k, const void *v, const void *out, const float *lse,
+                 const int32_t *cu_k, int32_t n_seqs, int32_t hq, int32_t hkv, int32_t d,
+                 int32_t dtype, int32_t mask, int32_t window, float scale,
+                 std::vector<int32_t> *cu_q) {
+  const int rc = check_decode_shape(cu_k, n_seqs, hq, hkv, d, dtype, mask, window, scale, cu_q);
+  if (rc != ATTN_OK) return rc;
+  int64_t Tq = 0, Tk = 0;
+  return check(q, k, v, out, lse, cu_q->data(), cu_k, n_seqs, hq, hkv, d, dtype, mask, window,
+               scale, &Tq, &Tk);
+}
+
 }  // namespace
 
 extern "C" {
@@ -186,6 +276,104 @@ int attn_prefill_kv(const void *q, const void *k, const void *v, void *out, floa
   if (rc != ATTN_OK || Tq == 0) return rc;
   return run(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, n_seqs, n_q_heads, n_kv_heads,
              head_dim, dtype, mask_kind, window, scale, stream);
+}
+
+int attn_decode_workspace_size(const int32_t *cu_seqlens_k, int32_t n_seqs, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                               int32_t mask_kind, int32_t window, uint64_t *bytes) {
+  if (bytes == nullptr) return ATTN_EINVAL;
+  std::vector<int32_t> cu_q;
+  const int rc = check_decode_shape(cu_seqlens_k, n_seqs, n_q_heads, n_kv_heads, head_dim, dtype,
+                                    mask_kind, window, 1.0f, &cu_q);
+  if (rc != ATTN_OK) return rc;
+  *bytes = 0;
+  if (n_seqs == 0 || !decode_fast(dtype, head_dim)) return ATTN_OK;
+  uint64_t total = 0;
+  for (int32_t base = 0; base < n_seqs; base += attn::kMaxDecodeSeqsPerLaunch) {
+    const int32_t cnt = std::min(n_seqs - base, attn::kMaxDecodeSeqsPerLaunch);
+    std::vector<int32_t> cu(cnt + 1);
+    for (int32_t i = 0; i <= cnt; ++i) cu[i] = cu_seqlens_k[base + i] - cu_seqlens_k[base];
+    const DecodePlan p = plan_decode(cu.data(), cnt, n_q_heads, n_kv_heads, mask_kind, window);
+    total = std::max(total, decode_workspace_bytes(p, head_dim));
+  }
+  *bytes = total;
+  return ATTN_OK;
+}
+
+int attn_decode(const void *q, const void *k, const void *v, void *out, float *lse,
+                const int32_t *cu_seqlens_k, int32_t n_seqs, int32_t n_q_heads,
+                int32_t n_kv_heads, int32_t head_dim, int32_t dtype, int32_t mask_kind,
+                int32_t window, float scale, void *workspace, uint64_t workspace_bytes,
+                void *stream) {
+  std::vector<int32_t> cu_q;
+  int rc = check_decode(q, k, v, out, lse, cu_seqlens_k, n_seqs, n_q_heads, n_kv_heads, head_dim,
+                        dtype, mask_kind, window, scale, &cu_q);
+  if (rc != ATTN_OK || n_seqs == 0) return rc;
+  if (!decode_fast(dtype, head_dim))
+    return run(q, k, v, out, lse, cu_q.data(), cu_seqlens_k, n_seqs, n_q_heads, n_kv_heads,
+               head_dim, dtype, mask_kind, window, scale, stream);
+  // plan every launch (at most kMaxDecodeSeqsPerLaunch sequences each; they
+  // run one after another on the stream and reuse the workspace) before any
+  std::vector<attn::DecodeArgs> plan;
+  const size_t es = 2;
+  for (int32_t base = 0; base < n_seqs; base += attn::kMaxDecodeSeqsPerLaunch) {
+    const int32_t cnt = std::min(n_seqs - base, attn::kMaxDecodeSeqsPerLaunch);
+    std::vector<int32_t> cu(cnt + 1);
+    for (int32_t i = 0; i <= cnt; ++i) cu[i] = cu_seqlens_k[base + i] - cu_seqlens_k[base];
+    const DecodePlan p = plan_decode(cu.data(), cnt, n_q_heads, n_kv_heads, mask_kind, window);
+    if (p.total_items > INT32_MAX) return ATTN_EUNSUPPORTED;
+    const uint64_t need = decode_workspace_bytes(p, head_dim);
+    if (need > 0) {
+      if (workspace == nullptr || workspace_bytes < need ||
+          (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+        return ATTN_EINVAL;
+      const uint64_t nq = static_cast<uint64_t>(n_seqs) * n_q_heads * head_dim * es;
+      const uint64_t nkv = static_cast<uint64_t>(cu_seqlens_k[n_seqs]) * n_kv_heads * head_dim * es;
+      const uint64_t nl = static_cast<uint64_t>(n_seqs) * n_q_heads * sizeof(float);
+      if (overlaps(workspace, need, q, nq) || overlaps(workspace, need, k, nkv) ||
+          overlaps(workspace, need, v, nkv) || overlaps(workspace, need, out, nq) ||
+          (lse != nullptr && overlaps(workspace, need, lse, nl)))
+        return ATTN_EINVAL;
+    }
+    attn::DecodeArgs a{};
+    const size_t qrow = static_cast<size_t>(n_q_heads) * head_dim * es;
+    a.q = static_cast<const char *>(q) + static_cast<size_t>(base) * qrow;
+    a.k = k;
+    a.v = v;
+    a.out = static_cast<char *>(out) + static_cast<size_t>(base) * qrow;
+    a.lse = lse == nullptr ? nullptr : lse + static_cast<size_t>(base) * n_q_heads;
+    // partial outputs first (16-byte rows), then the references and sums
+    a.ws_o = p.direct ? nullptr : static_cast<float *>(workspace);
+    a.ws_ml = p.direct ? nullptr
+                       : static_cast<float *>(workspace) +
+                             static_cast<size_t>(p.total_items) * p.rows * head_dim;
+    a.hq = n_q_heads;
+    a.hkv = n_kv_heads;
+    a.group = n_q_heads / n_kv_heads;
+    a.head_blocks = p.head_blocks;
+    a.rows = p.rows;
+    a.chunk = p.chunk;
+    a.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
+    a.n_seqs = cnt;
+    a.total_items = static_cast<int32_t>(p.total_items);
+    a.direct = p.direct ? 1 : 0;
+    int64_t item = 0;
+    for (int32_t i = 0; i < cnt; ++i) {
+      const int32_t b = base + i;
+      const int64_t n = cu_seqlens_k[b + 1] - cu_seqlens_k[b];
+      const int64_t lo = decode_lo(mask_kind, window, n);
+      a.k_begin[i] = static_cast<int32_t>(cu_seqlens_k[b] + lo);
+      a.k_count[i] = static_cast<int32_t>(n - lo);
+      a.splits[i] = static_cast<int32_t>((n - lo + p.chunk - 1) / p.chunk);
+      a.item_start[i] = static_cast<int32_t>(item);
+      item += static_cast<int64_t>(a.splits[i]) * n_kv_heads * p.head_blocks;
+    }
+    a.item_start[cnt] = static_cast<int32_t>(item);
+    plan.push_back(a);
+  }
+  for (const attn::DecodeArgs &a : plan)
+    if (attn::launch_decode_bf16(a, head_dim, stream) != 0) return ATTN_ELAUNCH;
+  return ATTN_OK;
 }
 
 const char *attn_strerror(int status) {

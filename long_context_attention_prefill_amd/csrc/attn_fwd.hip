@@ -1099,6 +1099,236 @@ __global__ __launch_bounds__(256) void fwd_f32(const LaunchArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode: one query per sequence over its key/value cache.  Every wave is an
+// independent worker on one item (sequence, KV head, block of up to 32 of
+// that KV head's query heads, chunk of up to a.chunk visible keys): the
+// block's query heads are the 32 query columns of S^T = K Q^T (unused columns
+// carry zeros), so each K and V element the item streams is used by all its
+// query heads.  32-key tiles reach the wave's own double-buffered LDS region
+// by direct loads in the prefill kernels' layout (rows of CH+1 16-byte slots,
+// permuted keys, transposing V reads), and the wave waits only on its own
+// loads.  The softmax is the online one (running maximum, rescale).  With one
+// chunk per (sequence, head block) the wave writes the output; otherwise it
+// writes its unnormalised output, reference and sum to the workspace and
+// decode_merge combines the chunks.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void decode_bf16_partial(const DecodeArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(D == 64 || D == 128, "decode covers head_dim 64 and 128");
+  using L = FastLayout<D>;
+  constexpr int BN = kDecodeTile;
+  constexpr int CH = L::CH;
+  constexpr int KST = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int NLOADS = (BN * L::SLOTS + 63) / 64;  // wave-wide loads per tile
+  constexpr int TILE = NLOADS * 1024;                // tile bytes, with zero-filled spill
+  // one array per (buffer half, tensor), indexed by wave: a direct load into
+  // one half is then visibly unrelated to reads of the other
+  __shared__ __attribute__((aligned(1024))) char k_lds0[4][TILE];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[4][TILE];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[4][TILE];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[4][TILE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __builtin_assume(wave >= 0 && wave < 4);
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int item = blockIdx.x * 4 + wave;
+  if (item >= a.total_items) return;  // a whole wave; no barrier follows
+
+  int seq = 0;
+  while (seq + 1 < a.n_seqs && a.item_start[seq + 1] <= item) ++seq;
+  const int rem = item - a.item_start[seq];
+  const int splits = a.splits[seq];
+  const int gh = rem / splits;
+  const int split = rem - gh * splits;
+  const int kvh = gh / a.head_blocks;
+  const int hb = gh - kvh * a.head_blocks;
+  const int k0 = split * a.chunk;                       // within the visible keys
+  const int k1 = min(k0 + a.chunk, a.k_count[seq]);
+  const float c = a.c == 0.0f ? 0x1p-126f : a.c;
+
+  // query head of this lane's column
+  const int hr = hb * 32 + l32;                         // head within the KV group
+  const bool col_ok = l32 < a.rows && hr < a.group;
+  const int h = kvh * a.group + hr;
+  bf16x8 qf[KST];
+  {
+    const __bf16 *qrow = reinterpret_cast<const __bf16 *>(a.q) + ((size_t)seq * a.hq + (col_ok ? h : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk)
+      qf[kk] = col_ok ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * kk + 8 * g) : (bf16x8)((__bf16)0.0f);
+  }
+
+  const int rowbytes = a.hkv * D * 2;
+  uint32_t ld_off[NLOADS];
+#pragma unroll
+  for (int j = 0; j < NLOADS; ++j) {
+    const int p = j * 64 + lane;
+    const int r = p / L::SLOTS, cs = p % L::SLOTS;
+    ld_off[j] = (cs < CH && r < BN) ? (uint32_t)(r * rowbytes + cs * 16) : kOutOfRange;
+  }
+  const size_t base = ((size_t)(a.k_begin[seq]) * a.hkv + kvh) * D * 2;
+  const char *kseq = reinterpret_cast<const char *>(a.k) + base;
+  const char *vseq = reinterpret_cast<const char *>(a.v) + base;
+  auto issue = [&](const char *src, char *lds, int kt) {
+    const int nrows = min(k1 - kt, BN);
+    const int rec = max(0, (nrows - 1) * rowbytes + D * 2);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(src + (size_t)kt * rowbytes), (short)0, rec, kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < NLOADS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(lds + j * 1024), 16, ld_off[j], 0, 0, 0);
+  };
+  auto issue_tile = [&](auto buf_tag, int kt) {
+    if constexpr (decltype(buf_tag)::value == 0) {
+      issue(kseq, k_lds0[wave], kt);
+      issue(vseq, v_lds0[wave], kt);
+    } else {
+      issue(kseq, k_lds1[wave], kt);
+      issue(vseq, v_lds1[wave], kt);
+    }
+  };
+  const int kread = key_of_row(l32) * L::ROWB + 16 * g;
+  const int vread = (g + 4 * ((lane & 15) >> 2)) * L::ROWB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16)(0.0f);
+  float m_run = kNegInf, l_run = 0.0f;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  auto step = [&](auto buf_tag, int kt) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    const char *kb = (BUF == 0 ? k_lds0[wave] : k_lds1[wave]) + kread;
+    const char *vb = (BUF == 0 ? v_lds0[wave] : v_lds1[wave]) + vread;
+    if (kt + BN < k1) issue_tile(std::integral_constant<int, BUF ^ 1>{}, kt + BN);
+    f32x16 sc = (f32x16)(0.0f);
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + kk * 32);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc, 0, 0, 0);
+    }
+    // x = c * s in exp2 units; keys past the chunk are void.  Entry j of
+    // lane half g holds key kt + 16 (j >> 3) + 2 ((j >> 2) & 1) + 4 (j & 3) + g.
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int key = kt + 16 * (j >> 3) + 2 * ((j >> 2) & 1) + 4 * (j & 3) + g;
+      sc[j] = key < k1 ? sc[j] * c : kNegInf;
+      mx = fmaxf(mx, sc[j]);
+    }
+    const float m_new = fmaxf(m_run, fmaxf(mx, xor32(mx)));
+    const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    m_run = m_new;
+    bf16x8 pf[BN / 16];
+#pragma unroll
+    for (int ks = 0; ks < BN / 16; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)fast_exp2(sc[8 * ks + e] - m_run);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {pf[ks][2 * e], pf[ks][2 * e + 1]};
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < BN / 16; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const char *vp = vb + ks * 16 * L::ROWB + db * 64;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp + 2 * L::ROWB));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
+      }
+    // the next tile's loads (into the other half) complete before it is read,
+    // and this half's reads complete before the tile after it overwrites it
+    __builtin_amdgcn_s_waitcnt(0);
+  };
+
+  issue_tile(std::integral_constant<int, 0>{}, k0);
+  __builtin_amdgcn_s_waitcnt(0);
+  int kt = k0;
+  for (; kt + BN < k1; kt += 2 * BN) {
+    step(std::integral_constant<int, 0>{}, kt);
+    step(std::integral_constant<int, 1>{}, kt + BN);
+  }
+  if (kt < k1) step(std::integral_constant<int, 0>{}, kt);
+
+  const float l_tot = l_run + xor32(l_run);
+  if (!col_ok) return;
+  if (a.direct) {
+    const float inv = 1.0f / l_tot;
+    __bf16 *orow = reinterpret_cast<__bf16 *>(a.out) + ((size_t)seq * a.hq + h) * D;
+    if (a.lse != nullptr && g == 0) a.lse[(size_t)seq * a.hq + h] = (m_run + log2f(l_tot)) * kLn2;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * jj + e] * inv);
+        *reinterpret_cast<bf16x4 *>(orow + 32 * db + 8 * jj + 4 * g) = w;
+      }
+  } else {
+    const size_t row = (size_t)item * a.rows + l32;
+    float *orow = a.ws_o + row * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = o[db][4 * jj + e];
+        *reinterpret_cast<f32x4 *>(orow + 32 * db + 8 * jj + 4 * g) = w;
+      }
+    if (g == 0) {
+      a.ws_ml[2 * row] = m_run;
+      a.ws_ml[2 * row + 1] = l_tot;
+    }
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// Merge of the chunks of one (sequence, query head): with references m_s and
+// sums l_s, m = max m_s, l = sum l_s 2^(m_s - m), out = sum o_s 2^(m_s - m) / l.
+template <int D>
+__global__ __launch_bounds__(64) void decode_merge(const DecodeArgs a) {
+  const int seq = blockIdx.x / a.hq;
+  const int h = blockIdx.x - seq * a.hq;
+  const int kvh = h / a.group;
+  const int hr = h - kvh * a.group;
+  const int hb = hr >> 5;
+  const int r = hr & 31;
+  const int splits = a.splits[seq];
+  const size_t first = (size_t)a.item_start[seq] + (size_t)(kvh * a.head_blocks + hb) * splits;
+  float m = kNegInf;
+  for (int s = 0; s < splits; ++s) m = fmaxf(m, a.ws_ml[2 * ((first + s) * a.rows + r)]);
+  float l = 0.0f;
+  for (int s = 0; s < splits; ++s) {
+    const size_t row = (first + s) * a.rows + r;
+    l += a.ws_ml[2 * row + 1] * fast_exp2(a.ws_ml[2 * row] - m);
+  }
+  const float inv = 1.0f / l;
+  for (int dd = threadIdx.x; dd < D; dd += 64) {
+    float acc = 0.0f;
+    for (int s = 0; s < splits; ++s) {
+      const size_t row = (first + s) * a.rows + r;
+      acc += a.ws_o[row * D + dd] * fast_exp2(a.ws_ml[2 * row] - m);
+    }
+    reinterpret_cast<__bf16 *>(a.out)[((size_t)seq * a.hq + h) * D + dd] = (__bf16)(acc * inv);
+  }
+  if (a.lse != nullptr && threadIdx.x == 0) a.lse[(size_t)seq * a.hq + h] = (m + log2f(l)) * kLn2;
+}
+
 template <typename K>
 int launch(K kernel, const LaunchArgs &a, int threads, void *stream) {
   void *args[] = {const_cast<LaunchArgs *>(&a)};
@@ -1120,6 +1350,28 @@ int launch_bf16(const LaunchArgs &a, int head_dim, void *stream) {
     case 72: return launch(fwd_bf16_generic<72, kWavesBf16>, a, kWavesBf16 * 64, stream);
     case 128: return launch(fwd_bf16_fast<128, kWavesBf16, 1>, a, kWavesBf16 * 64, stream);
     default: return static_cast<int>(hipErrorInvalidValue);
+  }
+}
+
+int launch_decode_bf16(const DecodeArgs &a, int head_dim, void *stream) {
+  if (a.total_items == 0) return 0;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  void *args[] = {const_cast<DecodeArgs *>(&a)};
+  const dim3 grid((a.total_items + 3) / 4), merge_grid(a.n_seqs * a.hq);
+  hipError_t e;
+  switch (head_dim) {
+    case 64:
+      e = hipLaunchKernel(reinterpret_cast<const void *>(decode_bf16_partial<64>), grid, dim3(256), args, 0, st);
+      if (e == hipSuccess && !a.direct)
+        e = hipLaunchKernel(reinterpret_cast<const void *>(decode_merge<64>), merge_grid, dim3(64), args, 0, st);
+      return static_cast<int>(e);
+    case 128:
+      e = hipLaunchKernel(reinterpret_cast<const void *>(decode_bf16_partial<128>), grid, dim3(256), args, 0, st);
+      if (e == hipSuccess && !a.direct)
+        e = hipLaunchKernel(reinterpret_cast<const void *>(decode_merge<128>), merge_grid, dim3(64), args, 0, st);
+      return static_cast<int>(e);
+    default:
+      return static_cast<int>(hipErrorInvalidValue);
   }
 }
 

@@ -47,9 +47,43 @@ struct LaunchArgs {
   int32_t level_start[kMaxSeqsPerLaunch + 1];
 };
 
+// Decode: one query (the newest token) per sequence against its key/value
+// cache.  An item is (sequence, KV head, block of up to 32 of its query heads,
+// chunk of the visible keys); one wave computes an item.  Sequences of a
+// launch are consecutive in the call.
+constexpr int kMaxDecodeSeqsPerLaunch = 64;
+constexpr int kDecodeTile = 32;  // keys per MFMA tile; chunks are multiples of it
+
+struct DecodeArgs {
+  const void *q;       // [n_seqs][hq][d], the launch's first sequence at row 0
+  const void *k;       // [Tk][hkv][d], packed over the whole call
+  const void *v;
+  void *out;           // [n_seqs][hq][d], same rows as q
+  float *lse;          // [n_seqs][hq] or null
+  float *ws_o;         // [total_items][rows][d] unnormalised partial outputs (split mode)
+  float *ws_ml;        // [total_items][rows][2]: exp2-unit reference and sum (split mode)
+  int32_t hq;
+  int32_t hkv;
+  int32_t group;       // hq / hkv
+  int32_t head_blocks; // ceil(group / 32)
+  int32_t rows;        // min(group, 32): query heads per item
+  int32_t chunk;       // keys per item, a multiple of kDecodeTile
+  float c;             // scale * log2(e)
+  int32_t n_seqs;
+  int32_t total_items;
+  int32_t direct;      // 1: one chunk per (sequence, head block): write out directly
+  int32_t k_begin[kMaxDecodeSeqsPerLaunch];     // packed index of the first visible key
+  int32_t k_count[kMaxDecodeSeqsPerLaunch];     // visible keys, >= 1
+  int32_t splits[kMaxDecodeSeqsPerLaunch];      // ceil(k_count / chunk)
+  int32_t item_start[kMaxDecodeSeqsPerLaunch + 1];
+};
+
 // Kernel families.  Each returns 0 or a hipError_t value.
 int launch_bf16(const LaunchArgs &a, int head_dim, void *stream);
 int launch_f32(const LaunchArgs &a, int head_dim, void *stream);
+// Decode (bf16, head_dim 64 or 128): the partial kernel, then, in split
+// mode, the merge kernel; both on `stream`.
+int launch_decode_bf16(const DecodeArgs &a, int head_dim, void *stream);
 // Query rows per workgroup of each family (the planner tiles with it).
 int rows_per_workgroup_bf16(int head_dim);
 int rows_per_workgroup_f32(int head_dim);

@@ -149,3 +149,48 @@ def test_kv_rejects_before_any_device_work(lib):
     z = (ctypes.c_int32 * 2)(0, 0)
     assert lib.attn_prefill_kv(0, K, V, 0, 0, z, ak, 1, 4, 2, 128, 1, 0, 0, ctypes.c_float(0.1),
                                None) == 0
+
+
+# ---------------------------------------------------------------- attn_decode
+
+def ws_size(lib, cu_k=(0, 10, 3000), hq=16, hkv=2, d=128, dtype=1, mask=0, window=0, n_seqs=None):
+    ak = (ctypes.c_int32 * len(cu_k))(*cu_k)
+    out = ctypes.c_uint64(0)
+    if n_seqs is None:
+        n_seqs = len(cu_k) - 1
+    st = lib.attn_decode_workspace_size(ak, n_seqs, hq, hkv, d, dtype, mask, window, ctypes.byref(out))
+    return st, out.value
+
+
+def test_decode_workspace_size(lib):
+    st, n = ws_size(lib)
+    assert st == lcap.ATTN_OK and n > 0
+    # one 32-key chunk per sequence: written directly, no workspace
+    assert ws_size(lib, cu_k=(0, 1, 33, 65)) == (lcap.ATTN_OK, 0)
+    # fp32 and head_dim 72 run through the prefill path
+    assert ws_size(lib, dtype=2) == (lcap.ATTN_OK, 0)
+    assert ws_size(lib, d=72) == (lcap.ATTN_OK, 0)
+    # the size grows with the cache
+    assert ws_size(lib, cu_k=(0, 100000))[1] >= ws_size(lib, cu_k=(0, 1000))[1]
+    for bad in (dict(cu_k=(0, 0, 10)), dict(cu_k=(1, 10)), dict(hq=3, hkv=2), dict(mask=2),
+                dict(n_seqs=-1)):
+        assert ws_size(lib, **bad)[0] == lcap.ATTN_EINVAL, bad
+    assert ws_size(lib, d=96)[0] == lcap.ATTN_EUNSUPPORTED
+
+
+def test_decode_rejects_before_any_device_work(lib):
+    ak = (ctypes.c_int32 * 3)(0, 10, 3000)
+    st, need = ws_size(lib)
+    W_ = 0x60000000
+
+    def call(ws, nbytes, q=Q, o=O, cu=ak):
+        return lib.attn_decode(q, K, V, o, None, cu, 2, 16, 2, 128, 1, 0, 0, ctypes.c_float(0.1),
+                               ws, nbytes, None)
+    assert call(None, 0) == lcap.ATTN_EINVAL            # workspace needed
+    assert call(W_, need - 16) == lcap.ATTN_EINVAL      # too small
+    assert call(W_ + 8, need) == lcap.ATTN_EINVAL       # misaligned
+    assert call(K, need) == lcap.ATTN_EINVAL            # overlaps k
+    empty = (ctypes.c_int32 * 3)(0, 10, 10)
+    assert call(W_, need, cu=empty) == lcap.ATTN_EINVAL  # a sequence without keys
+    assert lib.attn_decode(0, 0, 0, 0, None, None, 0, 16, 2, 128, 1, 0, 0, ctypes.c_float(0.1),
+                           None, 0, None) == 0
