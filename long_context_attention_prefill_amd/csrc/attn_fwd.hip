@@ -1105,17 +1105,21 @@ __global__ __launch_bounds__(256) void fwd_f32(const LaunchArgs a) {
 // that KV head's query heads, chunk of up to a.chunk visible keys): the
 // block's query heads are the 32 query columns of S^T = K Q^T (unused columns
 // carry zeros), so each K and V element the item streams is used by all its
-// query heads.  32-key tiles reach the wave's own double-buffered LDS region
-// by direct loads in the prefill kernels' layout (rows of CH+1 16-byte slots,
-// permuted keys, transposing V reads), and the wave waits only on its own
-// loads.  The softmax is the online one (running maximum, rescale).  With one
-// chunk per (sequence, head block) the wave writes the output; otherwise it
-// writes its unnormalised output, reference and sum to the workspace and
-// decode_merge combines the chunks.
+// query heads.  Per 32-key tile, K fragments come straight from memory into
+// registers (a range-checked buffer load per MFMA step: each lane reads 16
+// bytes of the key row it multiplies, keys past the chunk read as zeros),
+// one tile ahead; V reaches the wave's own double-buffered LDS region by
+// direct loads in the prefill layout (rows of CH+1 16-byte slots, permuted
+// keys) for the transposing reads.  A wave waits only on its own loads, and
+// two workgroups share a CU.  The softmax is the online one with the
+// prefill kernels' lazy rescale (the reference rises only by more than
+// kRescaleSlack doublings).  With one chunk per (sequence, head block) the
+// wave writes the output; otherwise it writes its unnormalised output,
+// reference and sum to the workspace and decode_merge combines the chunks.
 // ---------------------------------------------------------------------------
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void decode_bf16_partial(const DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_bf16_partial(const DecodeArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert(D == 64 || D == 128, "decode covers head_dim 64 and 128");
   using L = FastLayout<D>;
@@ -1123,12 +1127,10 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_partial(const DecodeArgs a
   constexpr int CH = L::CH;
   constexpr int KST = D / 16;
   constexpr int DB = D / 32;
-  constexpr int NLOADS = (BN * L::SLOTS + 63) / 64;  // wave-wide loads per tile
-  constexpr int TILE = NLOADS * 1024;                // tile bytes, with zero-filled spill
-  // one array per (buffer half, tensor), indexed by wave: a direct load into
-  // one half is then visibly unrelated to reads of the other
-  __shared__ __attribute__((aligned(1024))) char k_lds0[4][TILE];
-  __shared__ __attribute__((aligned(1024))) char k_lds1[4][TILE];
+  constexpr int NLOADS = (BN * L::SLOTS + 63) / 64;  // wave-wide V loads per tile
+  constexpr int TILE = NLOADS * 1024;                // V tile bytes, with zero-filled spill
+  // one array per buffer half, indexed by wave: a direct load into one half
+  // is then visibly unrelated to reads of the other
   __shared__ __attribute__((aligned(1024))) char v_lds0[4][TILE];
   __shared__ __attribute__((aligned(1024))) char v_lds1[4][TILE];
 
@@ -1175,59 +1177,77 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_partial(const DecodeArgs a
   const size_t base = ((size_t)(a.k_begin[seq]) * a.hkv + kvh) * D * 2;
   const char *kseq = reinterpret_cast<const char *>(a.k) + base;
   const char *vseq = reinterpret_cast<const char *>(a.v) + base;
-  auto issue = [&](const char *src, char *lds, int kt) {
+  // keys kt .. kt+31, rows past k1 out of range
+  auto tile_rsrc = [&](const char *src, int kt) {
     const int nrows = min(k1 - kt, BN);
     const int rec = max(0, (nrows - 1) * rowbytes + D * 2);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(src + (size_t)kt * rowbytes), (short)0, rec, kBufferWord3);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(src + (size_t)kt * rowbytes), (short)0,
+                                             rec, kBufferWord3);
+  };
+  auto issue_v = [&](auto buf_tag, int kt) {
+    char *lds = decltype(buf_tag)::value == 0 ? v_lds0[wave] : v_lds1[wave];
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vseq, kt);
 #pragma unroll
     for (int j = 0; j < NLOADS; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(lds + j * 1024), 16, ld_off[j], 0, 0, 0);
   };
-  auto issue_tile = [&](auto buf_tag, int kt) {
-    if constexpr (decltype(buf_tag)::value == 0) {
-      issue(kseq, k_lds0[wave], kt);
-      issue(vseq, v_lds0[wave], kt);
-    } else {
-      issue(kseq, k_lds1[wave], kt);
-      issue(vseq, v_lds1[wave], kt);
-    }
+  // K fragment kk of MFMA row l32 (key key_of_row(l32), the order the V
+  // reads expect): 16 bytes at column 16 kk + 8 g
+  const uint32_t kvoff = (uint32_t)(key_of_row(l32) * rowbytes + 16 * g);
+  auto load_k = [&](bf16x8 (&kf)[KST], int kt) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kseq, kt);
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk)
+      kf[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, kvoff + kk * 32, 0, 0));
   };
-  const int kread = key_of_row(l32) * L::ROWB + 16 * g;
   const int vread = (g + 4 * ((lane & 15) >> 2)) * L::ROWB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = (f32x16)(0.0f);
-  float m_run = kNegInf, l_run = 0.0f;
+  float m_run = kNegInf, l_run = 0.0f;  // reference (exp2 units) and this lane's share of the sum
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  bf16x8 kfa[KST], kfb[KST];
 
-  auto step = [&](auto buf_tag, int kt) __attribute__((always_inline)) {
+  // One tile: K in kf, V in buffer BUF; the next tile's K goes to kn and its
+  // V to the other buffer while this one is computed.
+  auto step = [&](auto buf_tag, bf16x8 (&kf)[KST], bf16x8 (&kn)[KST], int kt) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value;
-    const char *kb = (BUF == 0 ? k_lds0[wave] : k_lds1[wave]) + kread;
     const char *vb = (BUF == 0 ? v_lds0[wave] : v_lds1[wave]) + vread;
-    if (kt + BN < k1) issue_tile(std::integral_constant<int, BUF ^ 1>{}, kt + BN);
+    const bool more = kt + BN < k1;
+    if (more) {
+      issue_v(std::integral_constant<int, BUF ^ 1>{}, kt + BN);
+      load_k(kn, kt + BN);
+    }
     f32x16 sc = (f32x16)(0.0f);
 #pragma unroll
-    for (int kk = 0; kk < KST; ++kk) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + kk * 32);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], sc, 0, 0, 0);
-    }
-    // x = c * s in exp2 units; keys past the chunk are void.  Entry j of
-    // lane half g holds key kt + 16 (j >> 3) + 2 ((j >> 2) & 1) + 4 (j & 3) + g.
+    for (int kk = 0; kk < KST; ++kk) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], sc, 0, 0, 0);
+    // x = c * s in exp2 units; on the chunk's last tile keys past k1 are void.
+    // Entry j of lane half g holds key kt + 16 (j >> 3) + 2 ((j >> 2) & 1) + 4 (j & 3) + g.
     float mx = kNegInf;
+    if (kt + BN <= k1) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int key = kt + 16 * (j >> 3) + 2 * ((j >> 2) & 1) + 4 * (j & 3) + g;
-      sc[j] = key < k1 ? sc[j] * c : kNegInf;
-      mx = fmaxf(mx, sc[j]);
+      for (int j = 0; j < 16; ++j) {
+        sc[j] *= c;
+        mx = fmaxf(mx, sc[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = kt + 16 * (j >> 3) + 2 * ((j >> 2) & 1) + 4 * (j & 3) + g;
+        sc[j] = key < k1 ? sc[j] * c : kNegInf;
+        mx = fmaxf(mx, sc[j]);
+      }
     }
-    const float m_new = fmaxf(m_run, fmaxf(mx, xor32(mx)));
-    const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile
-    l_run *= alpha;
+    mx = fmaxf(mx, xor32(mx));
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack)) {
+      const float m_new = mx > m_run + kRescaleSlack ? mx : m_run;
+      const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile
+      l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    m_run = m_new;
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
     bf16x8 pf[BN / 16];
 #pragma unroll
     for (int ks = 0; ks < BN / 16; ++ks) {
@@ -1249,19 +1269,20 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_partial(const DecodeArgs a
         const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
       }
-    // the next tile's loads (into the other half) complete before it is read,
-    // and this half's reads complete before the tile after it overwrites it
+    // the next tile's loads complete before it is computed, and this V
+    // buffer's reads complete before the tile after next overwrites it
     __builtin_amdgcn_s_waitcnt(0);
   };
 
-  issue_tile(std::integral_constant<int, 0>{}, k0);
+  issue_v(std::integral_constant<int, 0>{}, k0);
+  load_k(kfa, k0);
   __builtin_amdgcn_s_waitcnt(0);
   int kt = k0;
   for (; kt + BN < k1; kt += 2 * BN) {
-    step(std::integral_constant<int, 0>{}, kt);
-    step(std::integral_constant<int, 1>{}, kt + BN);
+    step(std::integral_constant<int, 0>{}, kfa, kfb, kt);
+    step(std::integral_constant<int, 1>{}, kfb, kfa, kt + BN);
   }
-  if (kt < k1) step(std::integral_constant<int, 0>{}, kt);
+  if (kt < k1) step(std::integral_constant<int, 0>{}, kfa, kfb, kt);
 
   const float l_tot = l_run + xor32(l_run);
   if (!col_ok) return;
@@ -1300,8 +1321,16 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_partial(const DecodeArgs a
 
 // Merge of the chunks of one (sequence, query head): with references m_s and
 // sums l_s, m = max m_s, l = sum l_s 2^(m_s - m), out = sum o_s 2^(m_s - m) / l.
+// A sequence with few heads has many chunks, so 256 threads share them: each
+// thread owns four output columns and every (256 / (D / 4))-th chunk, with
+// independent loads, and the partial sums meet in LDS.
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge(const DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_merge(const DecodeArgs a) {
+  constexpr int CPL = D / 4;       // threads per chunk row (four columns each)
+  constexpr int NG = 256 / CPL;    // chunk groups
+  __shared__ float red[256];
+  __shared__ f32x4 part[NG][CPL];
+  const int t = threadIdx.x;
   const int seq = blockIdx.x / a.hq;
   const int h = blockIdx.x - seq * a.hq;
   const int kvh = h / a.group;
@@ -1310,23 +1339,52 @@ __global__ __launch_bounds__(64) void decode_merge(const DecodeArgs a) {
   const int r = hr & 31;
   const int splits = a.splits[seq];
   const size_t first = (size_t)a.item_start[seq] + (size_t)(kvh * a.head_blocks + hb) * splits;
+  auto ml = [&](int s) { return reinterpret_cast<const float2 *>(a.ws_ml)[(first + s) * a.rows + r]; };
+
   float m = kNegInf;
-  for (int s = 0; s < splits; ++s) m = fmaxf(m, a.ws_ml[2 * ((first + s) * a.rows + r)]);
+  for (int s = t; s < splits; s += 256) m = fmaxf(m, ml(s).x);
+  red[t] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) red[t] = fmaxf(red[t], red[t + w]);
+    __syncthreads();
+  }
+  m = red[0];
+  __syncthreads();
   float l = 0.0f;
-  for (int s = 0; s < splits; ++s) {
+  for (int s = t; s < splits; s += 256) {
+    const float2 e = ml(s);
+    l += e.y * fast_exp2(e.x - m);
+  }
+  red[t] = l;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
+    __syncthreads();
+  }
+  l = red[0];
+
+  const int col = t % CPL, grp = t / CPL;
+  f32x4 acc = (f32x4)(0.0f);
+#pragma unroll 4
+  for (int s = grp; s < splits; s += NG) {
     const size_t row = (first + s) * a.rows + r;
-    l += a.ws_ml[2 * row + 1] * fast_exp2(a.ws_ml[2 * row] - m);
+    const float w = fast_exp2(ml(s).x - m);
+    acc += *reinterpret_cast<const f32x4 *>(a.ws_o + row * D + 4 * col) * w;
   }
-  const float inv = 1.0f / l;
-  for (int dd = threadIdx.x; dd < D; dd += 64) {
-    float acc = 0.0f;
-    for (int s = 0; s < splits; ++s) {
-      const size_t row = (first + s) * a.rows + r;
-      acc += a.ws_o[row * D + dd] * fast_exp2(a.ws_ml[2 * row] - m);
-    }
-    reinterpret_cast<__bf16 *>(a.out)[((size_t)seq * a.hq + h) * D + dd] = (__bf16)(acc * inv);
+  part[grp][col] = acc;
+  __syncthreads();
+  if (t < CPL) {
+    f32x4 sum = part[0][t];
+#pragma unroll
+    for (int g = 1; g < NG; ++g) sum += part[g][t];
+    const float inv = 1.0f / l;
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (__bf16)(sum[e] * inv);
+    *reinterpret_cast<bf16x4 *>(reinterpret_cast<__bf16 *>(a.out) + ((size_t)seq * a.hq + h) * D + 4 * t) = o;
   }
-  if (a.lse != nullptr && threadIdx.x == 0) a.lse[(size_t)seq * a.hq + h] = (m + log2f(l)) * kLn2;
+  if (a.lse != nullptr && t == 0) a.lse[(size_t)seq * a.hq + h] = (m + log2f(l)) * kLn2;
 }
 
 template <typename K>
@@ -1363,12 +1421,12 @@ int launch_decode_bf16(const DecodeArgs &a, int head_dim, void *stream) {
     case 64:
       e = hipLaunchKernel(reinterpret_cast<const void *>(decode_bf16_partial<64>), grid, dim3(256), args, 0, st);
       if (e == hipSuccess && !a.direct)
-        e = hipLaunchKernel(reinterpret_cast<const void *>(decode_merge<64>), merge_grid, dim3(64), args, 0, st);
+        e = hipLaunchKernel(reinterpret_cast<const void *>(decode_merge<64>), merge_grid, dim3(256), args, 0, st);
       return static_cast<int>(e);
     case 128:
       e = hipLaunchKernel(reinterpret_cast<const void *>(decode_bf16_partial<128>), grid, dim3(256), args, 0, st);
       if (e == hipSuccess && !a.direct)
-        e = hipLaunchKernel(reinterpret_cast<const void *>(decode_merge<128>), merge_grid, dim3(64), args, 0, st);
+        e = hipLaunchKernel(reinterpret_cast<const void *>(decode_merge<128>), merge_grid, dim3(256), args, 0, st);
       return static_cast<int>(e);
     default:
       return static_cast<int>(hipErrorInvalidValue);
