@@ -7,9 +7,12 @@ bf16 prefill of one 10240-token sequence, 16 query / 2 KV heads, head dim
 128, with the needle planted at 60 % depth.  Beside it, each at its own
 shape: causal 2048 tokens (16/16 heads), and the packed 4-sequence batch
 (2048 + 5120 + 8192 + 10240 tokens, 16/2 heads) under the causal and the
-256-token window mask.  Each of these is timed as >= 20 samples of R
-back-to-back calls (R chosen so a sample lasts >= 1 ms) between two events,
-reported per call as median / min / p90.  Prints ONE JSON line.
+256-token window mask; the 10k sequence prefilled in five 2048-query chunks
+over its growing cache (attn_prefill_kv); and decode (attn_decode) of one
+and of 64 newest tokens over 10240-token caches.  Each of these is timed as
+>= 20 samples of R back-to-back calls (R chosen so a sample lasts >= 1 ms)
+between two events, reported per call as median / min / p90.  Prints ONE
+JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only]
                     [--no-cpu-baseline] [--sweep] [--copy-calibration]
@@ -31,7 +34,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "long_context_attention_prefill_amd", "csrc", "attn_fwd.hip")
+# sources the prefill kernels are compiled from (the traffic summary names their digest)
+KERNEL_SRCS = [os.path.join(ROOT, "long_context_attention_prefill_amd", "csrc", f)
+               for f in ("attn_fwd.hip", "attn_device.h", "attn_launch.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_d128_causal_n10240.txt")
 
 
@@ -95,8 +100,8 @@ def time_calls(w, dev, cu, steps, warmup):
 
 
 def sample_calls(w, dev, cu, n_samples=20, min_ms=1.0):
-    """Per-call ms of n_samples samples, each R back-to-back calls between two
-    events on the launch stream, R chosen so one sample lasts >= min_ms."""
+    """Per-call ms of n_samples samples of attn_prefill on the workload (see
+    event_samples)."""
     import torch
 
     import long_context_attention_prefill_amd as lcap
@@ -104,24 +109,8 @@ def sample_calls(w, dev, cu, n_samples=20, min_ms=1.0):
     q, k, v = dev
     out = torch.empty_like(q)
     cu_l = [int(x) for x in cu]
-    stream = torch.cuda.current_stream()
-    for _ in range(5):
-        lcap.attn_prefill(q, k, v, cu_l, mask=w.mask, scale=w.scale, out=out)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    lcap.attn_prefill(q, k, v, cu_l, mask=w.mask, scale=w.scale, out=out)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    reps = max(1, int(math.ceil(min_ms / max(e0.elapsed_time(e1), 1e-3))))
-    per_call = []
-    for _ in range(n_samples):
-        e0.record(stream)
-        for _ in range(reps):
-            lcap.attn_prefill(q, k, v, cu_l, mask=w.mask, scale=w.scale, out=out)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        per_call.append(e0.elapsed_time(e1) / reps)
-    return np.array(per_call), reps
+    return event_samples(lambda: lcap.attn_prefill(q, k, v, cu_l, mask=w.mask, scale=w.scale,
+                                                   out=out), n_samples, min_ms)
 
 
 def summarize(w, per_call_ms, reps):
@@ -141,10 +130,100 @@ def summarize(w, per_call_ms, reps):
     return res
 
 
+def event_samples(fn, n_samples=20, min_ms=1.0):
+    """Per-call ms of fn(): n_samples samples of R back-to-back calls between
+    two events on the current stream, R chosen so a sample lasts >= min_ms."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for _ in range(5):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    reps = max(1, int(math.ceil(min_ms / max(e0.elapsed_time(e1), 1e-3))))
+    per_call = []
+    for _ in range(n_samples):
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_call.append(e0.elapsed_time(e1) / reps)
+    return np.array(per_call), reps
+
+
+def chunked_prefill(w, dev, chunk):
+    """The workload's single sequence prefilled in query chunks of `chunk`
+    tokens, each an attn_prefill_kv call over the cache so far (bottom-right
+    causal alignment): the same (query, key) pairs as one attn_prefill call."""
+    import long_context_attention_prefill_amd as lcap
+
+    assert len(w.seq_lens) == 1 and w.mask == "causal"
+    q, k, v = dev
+    import torch
+
+    out = torch.empty_like(q)
+    n = w.total_tokens
+    bounds = list(range(0, n, chunk)) + [n]
+
+    def step():
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            lcap.attn_prefill_kv(q[a:b], k[:b], v[:b], [0, b - a], [0, b], mask="causal",
+                                 scale=w.scale, out=out[a:b])
+
+    per_call, reps = event_samples(step)
+    flops, byts = algorithmic(w)
+    med = float(np.median(per_call))
+    return {"workload": f"{w.name}, as {len(bounds) - 1} query chunks of {chunk} over the growing "
+                        "cache (attn_prefill_kv)",
+            "ms_median": round(med, 5), "ms_min": round(float(per_call.min()), 5),
+            "ms_p90": round(float(np.percentile(per_call, 90)), 5),
+            "samples": int(per_call.size), "calls_per_sample": reps,
+            "tokens_per_s": round(n / (med * 1e-3), 1),
+            "tflops": round(flops / (med * 1e-3) / 1e12, 1),
+            "pct_bf16_peak": round(100 * flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+
+
+def decode_step(n_seqs, cache_len, hq, hkv, d=128, seed=0):
+    """attn_decode of n_seqs newest tokens over bf16 caches of cache_len tokens
+    each (seeded normal values): time per step and the HBM rate of its
+    algorithmic bytes (K and V of every cache read once, q read, out written)."""
+    import torch
+
+    import long_context_attention_prefill_amd as lcap
+
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    Tk = n_seqs * cache_len
+    q = torch.randn(n_seqs, hq, d, device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.randn(Tk, hkv, d, device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn(Tk, hkv, d, device="cuda", generator=g).to(torch.bfloat16)
+    cu = [i * cache_len for i in range(n_seqs + 1)]
+    need = lcap.attn_decode_workspace_size(cu, hq, hkv, d)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    per_call, reps = event_samples(lambda: lcap.attn_decode(q, k, v, cu, out=out, workspace=ws))
+    med = float(np.median(per_call))
+    byts = 2 * Tk * hkv * d * 2 + 2 * n_seqs * hq * d * 2
+    gbs = byts / (med * 1e-3) / 1e9
+    del q, k, v, ws, out
+    return {"workload": f"decode, {n_seqs} x {cache_len}-token cache, {hq}/{hkv} heads, d {d}, bf16",
+            "us_median": round(med * 1e3, 2), "us_min": round(float(per_call.min()) * 1e3, 2),
+            "us_p90": round(float(np.percentile(per_call, 90)) * 1e3, 2),
+            "samples": int(per_call.size), "calls_per_sample": reps,
+            "tokens_per_s": round(n_seqs / (med * 1e-3), 1),
+            "algorithmic_bytes": byts, "algorithmic_hbm_gbs": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
+
+
 def gpu_clock():
     """Current shader clock as rocm-smi reports it (best effort, text)."""
     import subprocess
 
+    if any(k.startswith("ROCPROF") for k in os.environ):
+        return None  # under a profiler the child's launcher may not exec
     try:
         r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
         for line in r.stdout.splitlines():
@@ -156,8 +235,11 @@ def gpu_clock():
 
 
 def kernel_digest():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
@@ -261,12 +343,17 @@ def main():
     others = {}
     if not args.headline_only:
         stats10 = summarize(w10, *sample_calls(w10, dev10, host10[3]))
+        others["chunked"] = chunked_prefill(w10, dev10, 2048)
         del dev10[:]
         for key in ("2", "5a", "5b"):
             w = W.WORKLOADS[key]
             hst, dv = device_inputs(w)
             others[key] = summarize(w, *sample_calls(w, dv, hst[3]))
             del dv
+        torch.cuda.empty_cache()
+        # decode over the cache a 10k prefill leaves: one sequence, and a batch
+        others["decode_1"] = decode_step(1, 10240, 16, 2)
+        others["decode_64"] = decode_step(64, 10240, 16, 2)
         torch.cuda.empty_cache()
 
     sweep = None
@@ -317,6 +404,9 @@ def main():
         line["at_2k"] = others["2"]
         line["packed_causal_5a"] = others["5a"]
         line["packed_window256_5b"] = others["5b"]
+        line["chunked_prefill_10k"] = others["chunked"]
+        line["decode_10k_cache_b1"] = others["decode_1"]
+        line["decode_10k_cache_b64"] = others["decode_64"]
         line["gpu_clock"] = gpu_clock()
     if sweep is not None:
         line["sweep_tflops_16x2_causal"] = sweep

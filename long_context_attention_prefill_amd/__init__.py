@@ -284,9 +284,10 @@ def attn_decode(q, k, v, cu_seqlens_k, mask="causal", scale=None, out=None, lse=
     cu_q = list(range(n + 1))
     a = _args_kv(q, k, v, out, lse_t, cu_q, cu_seqlens_k, mask, scale)
     qp, kp, vp_, op, lp, _, cu_k, n_seqs, hq, hkv, d, dt, kind, window, sc = a
-    need = attn_decode_workspace_size(cu_seqlens_k, hq, hkv, d, dt, mask)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        need = attn_decode_workspace_size(cu_seqlens_k, hq, hkv, d, dt, mask)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = None if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if stream is None:

@@ -1,8 +1,8 @@
 """Build the HIP library in-tree: ``python -m long_context_attention_prefill_amd.build``.
 
 Produces ``long_context_attention_prefill_amd/libattn_prefill.so`` for gfx950:
-the kernels (csrc/attn_fwd.hip) compiled by hipcc, the host-only C ABI
-(csrc/attn_api.cpp) compiled by g++, linked by hipcc.
+the kernels (csrc/attn_fwd.hip, csrc/attn_decode.hip) compiled by hipcc, the
+host-only C ABI (csrc/attn_api.cpp) compiled by g++, linked by hipcc.
 """
 from __future__ import annotations
 
@@ -17,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIBRARY = os.path.join(PKG, "libattn_prefill.so")
 ARCH = "gfx950"
+
+# Kernel sources: prefill (both families) and decode.
+DEVICE_SOURCES = ("attn_fwd.hip", "attn_decode.hip")
 
 # Packed-fp32 VALU forms are kept out of every kernel on purpose.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -40,14 +43,16 @@ def build(verbose: bool = False, output: str = LIBRARY, extra_device_flags=()) -
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     with tempfile.TemporaryDirectory() as tmp:
         api_o = os.path.join(tmp, "attn_api.o")
-        fwd_o = os.path.join(tmp, "attn_fwd.o")
         _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", *inc, "-c",
               os.path.join(CSRC, "attn_api.cpp"), "-o", api_o], verbose)
-        _run([hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", *DEVICE_FLAGS,
-              *extra_device_flags, *inc, "-c", os.path.join(CSRC, "attn_fwd.hip"), "-o", fwd_o],
-             verbose)
+        objs = []
+        for src in DEVICE_SOURCES:
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            _run([hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", *DEVICE_FLAGS,
+                  *extra_device_flags, *inc, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+            objs.append(obj)
         tmp_out = output + ".tmp"
-        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_out, fwd_o, api_o],
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_out, *objs, api_o],
              verbose)
         os.replace(tmp_out, output)
     return output

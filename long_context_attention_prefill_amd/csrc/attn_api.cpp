@@ -9,7 +9,7 @@
 #include <cstdint>
 #include <vector>
 
-#include "../../include/attn_prefill.h"
+#include "attn_prefill.h"
 #include "attn_launch.h"
 
 namespace {
@@ -161,8 +161,11 @@ int run(const void *q, const void *k, const void *v, void *out, float *lse,
 bool decode_fast(int32_t dtype, int32_t d) { return dtype == ATTN_BF16 && (d == 64 || d == 128); }
 
 // Workers to aim for: 256 CUs x 4 waves, twice over, so chunks stay short
-// enough to spread a small batch over the whole GPU.
+// enough to spread a small batch over the whole GPU; but no chunk shorter
+// than kDecodeMinTiles tiles, whose per-chunk costs (query load, partial
+// store, merge) would outweigh the keys they cover.
 constexpr int64_t kDecodeTargetItems = 2048;
+constexpr int64_t kDecodeMinTiles = 4;
 
 struct DecodePlan {
   int32_t chunk = attn::kDecodeTile;
@@ -190,7 +193,8 @@ DecodePlan plan_decode(const int32_t *cu_k, int32_t n_seqs, int32_t hq, int32_t 
   }
   tiles *= static_cast<int64_t>(hkv) * p.head_blocks;
   const int64_t per = (tiles + kDecodeTargetItems - 1) / kDecodeTargetItems;
-  p.chunk = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(per, 1 << 20)) * attn::kDecodeTile);
+  p.chunk = static_cast<int32_t>(std::max<int64_t>(kDecodeMinTiles, std::min<int64_t>(per, 1 << 20)) *
+                                 attn::kDecodeTile);
   for (int32_t b = 0; b < n_seqs; ++b) {
     const int64_t n = cu_k[b + 1] - cu_k[b];
     const int64_t vis = n - decode_lo(mask, window, n);
