@@ -238,23 +238,24 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_partial(const DecodeArgs a
 
 // Merge of the chunks of one (sequence, query head): with references m_s and
 // sums l_s, m = max m_s, l = sum l_s 2^(m_s - m), out = sum o_s 2^(m_s - m) / l.
-// A sequence with few heads has many chunks, so each workgroup takes 32
-// output columns of one (sequence, head): its 256 threads find m and l
-// together, then each thread owns four columns and every 32nd chunk, eight
-// independent loads at a time, and the partial sums meet in LDS.
-constexpr int kMergeCols = 32;
-
-template <int D>
+// A workgroup takes CB output columns of one (sequence, head): its 256
+// threads find m and l together (wave reductions, then one exchange), then
+// each thread owns four columns and every (256 / (CB / 4))-th chunk, eight
+// independent loads at a time, and the partial sums meet in LDS.  With few
+// (sequence, head) pairs (small batches, hence many chunks each) CB = 32
+// spreads one pair over D / 32 workgroups; otherwise CB = D.
+template <int D, int CB>
 __global__ __launch_bounds__(256) void decode_merge(const DecodeArgs a) {
-  static_assert(D % kMergeCols == 0, "whole column blocks");
-  constexpr int CPL = kMergeCols / 4;  // threads per chunk row (four columns each)
-  constexpr int NG = 256 / CPL;        // chunk groups
-  constexpr int U = 8;                 // loads in flight per thread
-  __shared__ float red[256];
+  static_assert(D % CB == 0 && CB % 32 == 0, "whole column blocks");
+  constexpr int CPL = CB / 4;  // threads per chunk row (four columns each)
+  constexpr int NG = 256 / CPL;  // chunk groups
+  constexpr int U = 8;           // loads in flight per thread
+  __shared__ float red[2][4];
   __shared__ f32x4 part[NG][CPL];
   const int t = threadIdx.x;
-  const int cb = blockIdx.x % (D / kMergeCols);
-  const int sh = blockIdx.x / (D / kMergeCols);
+  const int wave = t >> 6;
+  const int cb = blockIdx.x % (D / CB);
+  const int sh = blockIdx.x / (D / CB);
   const int seq = sh / a.hq;
   const int h = sh - seq * a.hq;
   const int kvh = h / a.group;
@@ -267,28 +268,21 @@ __global__ __launch_bounds__(256) void decode_merge(const DecodeArgs a) {
 
   float m = kNegInf;
   for (int s = t; s < splits; s += 256) m = fmaxf(m, ml(s).x);
-  red[t] = m;
+#pragma unroll
+  for (int w = 32; w > 0; w >>= 1) m = fmaxf(m, __shfl_xor(m, w));
+  if ((t & 63) == 0) red[0][wave] = m;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (t < w) red[t] = fmaxf(red[t], red[t + w]);
-    __syncthreads();
-  }
-  m = red[0];
-  __syncthreads();
+  m = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
   float l = 0.0f;
   for (int s = t; s < splits; s += 256) {
     const float2 e = ml(s);
     l += e.y * fast_exp2(e.x - m);
   }
-  red[t] = l;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (t < w) red[t] += red[t + w];
-    __syncthreads();
-  }
-  l = red[0];
+#pragma unroll
+  for (int w = 32; w > 0; w >>= 1) l += __shfl_xor(l, w);
+  if ((t & 63) == 0) red[1][wave] = l;
 
-  const int col = cb * kMergeCols + 4 * (t % CPL), grp = t / CPL;
+  const int col = cb * CB + 4 * (t % CPL), grp = t / CPL;
   f32x4 acc = (f32x4)(0.0f);
   for (int s0 = grp; s0 < splits; s0 += U * NG) {
     f32x4 ov[U];
@@ -308,6 +302,7 @@ __global__ __launch_bounds__(256) void decode_merge(const DecodeArgs a) {
   }
   part[grp][t % CPL] = acc;
   __syncthreads();
+  l = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
   if (t < CPL) {
     f32x4 sum = part[0][t];
 #pragma unroll
@@ -321,28 +316,39 @@ __global__ __launch_bounds__(256) void decode_merge(const DecodeArgs a) {
   if (a.lse != nullptr && cb == 0 && t == 0) a.lse[(size_t)seq * a.hq + h] = (m + log2f(l)) * kLn2;
 }
 
+// (sequence, head) pairs from which each pair gets one merge workgroup
+constexpr int kMergeWideFrom = 256;
+
 }  // namespace
 
 int launch_decode_bf16(const DecodeArgs &a, int head_dim, void *stream) {
   if (a.total_items == 0) return 0;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   void *args[] = {const_cast<DecodeArgs *>(&a)};
-  const dim3 grid((a.total_items + 3) / 4), merge_grid(a.n_seqs * a.hq * (head_dim / kMergeCols));
-  hipError_t e;
+  const dim3 grid((a.total_items + 3) / 4);
+  const int pairs = a.n_seqs * a.hq;
+  const bool wide = pairs >= kMergeWideFrom;
+  const void *partial, *merge;
   switch (head_dim) {
     case 64:
-      e = hipLaunchKernel(reinterpret_cast<const void *>(decode_bf16_partial<64>), grid, dim3(256), args, 0, st);
-      if (e == hipSuccess && !a.direct)
-        e = hipLaunchKernel(reinterpret_cast<const void *>(decode_merge<64>), merge_grid, dim3(256), args, 0, st);
-      return static_cast<int>(e);
+      partial = reinterpret_cast<const void *>(decode_bf16_partial<64>);
+      merge = wide ? reinterpret_cast<const void *>(decode_merge<64, 64>)
+                   : reinterpret_cast<const void *>(decode_merge<64, 32>);
+      break;
     case 128:
-      e = hipLaunchKernel(reinterpret_cast<const void *>(decode_bf16_partial<128>), grid, dim3(256), args, 0, st);
-      if (e == hipSuccess && !a.direct)
-        e = hipLaunchKernel(reinterpret_cast<const void *>(decode_merge<128>), merge_grid, dim3(256), args, 0, st);
-      return static_cast<int>(e);
+      partial = reinterpret_cast<const void *>(decode_bf16_partial<128>);
+      merge = wide ? reinterpret_cast<const void *>(decode_merge<128, 128>)
+                   : reinterpret_cast<const void *>(decode_merge<128, 32>);
+      break;
     default:
       return static_cast<int>(hipErrorInvalidValue);
   }
+  hipError_t e = hipLaunchKernel(partial, grid, dim3(256), args, 0, st);
+  if (e == hipSuccess && !a.direct) {
+    const dim3 merge_grid(pairs * (wide ? 1 : head_dim / 32));
+    e = hipLaunchKernel(merge, merge_grid, dim3(256), args, 0, st);
+  }
+  return static_cast<int>(e);
 }
 
 }  // namespace attn

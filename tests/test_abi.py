@@ -165,7 +165,7 @@ def ws_size(lib, cu_k=(0, 10, 3000), hq=16, hkv=2, d=128, dtype=1, mask=0, windo
 def test_decode_workspace_size(lib):
     st, n = ws_size(lib)
     assert st == lcap.ATTN_OK and n > 0
-    # one 32-key chunk per sequence: written directly, no workspace
+    # one chunk per sequence: written directly, no workspace
     assert ws_size(lib, cu_k=(0, 1, 33, 65)) == (lcap.ATTN_OK, 0)
     # fp32 and head_dim 72 run through the prefill path
     assert ws_size(lib, dtype=2) == (lcap.ATTN_OK, 0)

@@ -72,7 +72,7 @@ def test_decode_unusual_scales(orc, scale):
 
 
 def test_decode_direct_mode(orc):
-    """Caches of at most one 32-key chunk are written without the merge."""
+    """Caches that fit one chunk are written without the merge."""
     import long_context_attention_prefill_amd as lcap
 
     lens = [1, 5, 17, 32, 32, 2]
@@ -92,6 +92,15 @@ def test_decode_many_sequences(orc):
     rng = np.random.Generator(np.random.PCG64(8))
     lens = rng.integers(1, 600, 150).tolist()
     q, k, v, cu_k = _case(lens, 8, 1, 128, "bf16", seed=8)
+    _check(orc, q, k, v, cu_k, "causal", 1 / math.sqrt(128), "bf16")
+
+
+@pytest.mark.parametrize("lens,heads", [([131072], (8, 1)), ([32768], (256, 1))], ids=str)
+def test_decode_long_cache(orc, lens, heads):
+    """Hundreds of chunks per (sequence, head): the merge takes several passes
+    of loads, with one (sequence, head) per workgroup or spread over several."""
+    hq, hkv = heads
+    q, k, v, cu_k = _case(lens, hq, hkv, 128, "bf16", seed=12)
     _check(orc, q, k, v, cu_k, "causal", 1 / math.sqrt(128), "bf16")
 
 
