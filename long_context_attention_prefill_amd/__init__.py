@@ -13,6 +13,9 @@ functions carry the C entry points' names:
 * ``attn_prefill_check(...)``, ``attn_prefill_kv_check(...)``,
   ``attn_decode_workspace_size(...)``, ``attn_strerror(status)``,
   ``attn_version()``
+* ``gdn_prefill(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None,
+  out=None, final_state=False, workspace=None)`` -- chunked gated-delta-rule
+  prefill (include/gdn_prefill.h), and ``gdn_prefill_workspace_size(...)``
 
 There is no fallback: if the library is missing or cannot be loaded, the
 call raises.
@@ -25,6 +28,7 @@ import os
 
 __all__ = ["attn_prefill", "attn_prefill_check", "attn_prefill_kv", "attn_prefill_kv_check",
            "attn_decode", "attn_decode_workspace_size", "attn_strerror", "attn_version",
+           "gdn_prefill", "gdn_prefill_workspace_size",
            "AttnError", "library_path", "load_library", "ATTN_OK", "ATTN_EINVAL",
            "ATTN_EUNSUPPORTED", "ATTN_ELAUNCH", "ATTN_BF16", "ATTN_F32", "ATTN_CAUSAL",
            "ATTN_FULL", "ATTN_WINDOW"]
@@ -80,6 +84,16 @@ def load_library() -> ctypes.CDLL:
     lib.attn_decode_workspace_size.argtypes = [ip, i32, i32, i32, i32, i32, i32, i32,
                                                ctypes.POINTER(ctypes.c_uint64)]
     lib.attn_decode_workspace_size.restype = ctypes.c_int
+    fp = ctypes.c_void_p
+    lib.gdn_prefill.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, ip, i32, i32, i32, i32, i32,
+                                ctypes.c_float, vp, ctypes.c_uint64, vp]
+    lib.gdn_prefill.restype = ctypes.c_int
+    lib.gdn_prefill_check.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, ip, i32, i32, i32, i32,
+                                      i32, ctypes.c_float, vp, ctypes.c_uint64]
+    lib.gdn_prefill_check.restype = ctypes.c_int
+    lib.gdn_prefill_workspace_size.argtypes = [ip, i32, i32, i32, i32, i32,
+                                               ctypes.POINTER(ctypes.c_uint64)]
+    lib.gdn_prefill_workspace_size.restype = ctypes.c_int
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -298,3 +312,77 @@ def attn_decode(q, k, v, cu_seqlens_k, mask="causal", scale=None, out=None, lse=
     if status != ATTN_OK:
         raise AttnError(status, "attn_decode")
     return out if lse_t is None else (out, lse_t)
+
+
+def gdn_prefill_workspace_size(cu_seqlens, n_heads, head_dim_k=128, head_dim_v=128,
+                               dtype=ATTN_BF16) -> int:
+    """Workspace bytes gdn_prefill needs for this shape (host-only)."""
+    cu, n = _cu_array(cu_seqlens)
+    out = ctypes.c_uint64(0)
+    status = load_library().gdn_prefill_workspace_size(cu, n, int(n_heads), int(head_dim_k),
+                                                       int(head_dim_v), int(dtype),
+                                                       ctypes.byref(out))
+    if status != ATTN_OK:
+        raise AttnError(status, "gdn_prefill_workspace_size")
+    return int(out.value)
+
+
+def gdn_prefill(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None, out=None,
+                final_state=False, workspace=None, stream=None):
+    """Chunked gated-delta-rule prefill over a packed batch.
+
+    q, k: [T, H, dk] bf16; v: [T, H, dv] bf16; g (log decay) and beta:
+    [T, H] float32; initial_state: None or float32 [n_seqs, H, dv, dk].
+    ``final_state``: False (not computed), True (allocated and returned) or a
+    float32 tensor to fill (may be ``initial_state`` itself, updated in
+    place).  ``workspace``: a device tensor of at least
+    gdn_prefill_workspace_size(...) bytes, or None to allocate one here.
+    Returns ``out`` or ``(out, final_state)``.
+    """
+    import torch
+
+    lib = load_library()
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("q, k must be [T, H, dk] and v [T, H, dv]")
+    T, H, dk = (int(x) for x in q.shape)
+    dv = int(v.shape[2])
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if tuple(g.shape) != (T, H) or tuple(beta.shape) != (T, H):
+        raise ValueError("g and beta must be [T, H]")
+    if g.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise ValueError("g and beta must be float32")
+    cu, n = _cu_array(cu_seqlens)
+    if n >= 0 and int(cu[n]) != T:
+        raise ValueError("cu_seqlens[-1] must equal T")
+    if out is None:
+        out = torch.empty_like(v)
+    fin = None
+    if final_state is True:
+        fin = torch.empty((max(n, 0), H, dv, dk), dtype=torch.float32, device=q.device)
+    elif final_state is not False and final_state is not None:
+        fin = final_state
+    for name, t in (("initial_state", initial_state), ("final_state", fin)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (n, H, dv, dk)
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 [n_seqs, H, dv, dk] tensor")
+    if workspace is None:
+        need = gdn_prefill_workspace_size(cu_seqlens, H, dk, dv, _dtype_code(q))
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream or 0)
+    status = lib.gdn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                             beta.data_ptr(),
+                             None if initial_state is None else initial_state.data_ptr(),
+                             out.data_ptr(), None if fin is None else fin.data_ptr(), cu, n, H,
+                             dk, dv, _dtype_code(q), float(1.0 / math.sqrt(dk) if scale is None
+                                                           else scale),
+                             ws_ptr, ws_bytes, ctypes.c_void_p(handle))
+    if status != ATTN_OK:
+        raise AttnError(status, "gdn_prefill")
+    return out if fin is None else (out, fin)

@@ -1,8 +1,9 @@
 """Build the HIP library in-tree: ``python -m long_context_attention_prefill_amd.build``.
 
 Produces ``long_context_attention_prefill_amd/libattn_prefill.so`` for gfx950:
-the kernels (csrc/attn_fwd.hip, csrc/attn_decode.hip) compiled by hipcc, the
-host-only C ABI (csrc/attn_api.cpp) compiled by g++, linked by hipcc.
+the kernels (csrc/attn_fwd.hip, csrc/attn_decode.hip, csrc/gdn_fwd.hip)
+compiled by hipcc, the host-only C ABI (csrc/attn_api.cpp, csrc/gdn_api.cpp)
+compiled by g++, linked by hipcc.
 """
 from __future__ import annotations
 
@@ -18,8 +19,10 @@ ROOT = os.path.dirname(PKG)
 LIBRARY = os.path.join(PKG, "libattn_prefill.so")
 ARCH = "gfx950"
 
-# Kernel sources: prefill (both families) and decode.
-DEVICE_SOURCES = ("attn_fwd.hip", "attn_decode.hip")
+# Kernel sources: attention prefill (both families), decode, gated delta rule.
+DEVICE_SOURCES = ("attn_fwd.hip", "attn_decode.hip", "gdn_fwd.hip")
+# Host-only sources (C ABI: checks and planning), compiled by g++.
+HOST_SOURCES = ("attn_api.cpp", "gdn_api.cpp")
 
 # Packed-fp32 VALU forms are kept out of every kernel on purpose.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -42,18 +45,19 @@ def build(verbose: bool = False, output: str = LIBRARY, extra_device_flags=()) -
     hipcc = _hipcc()
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     with tempfile.TemporaryDirectory() as tmp:
-        api_o = os.path.join(tmp, "attn_api.o")
-        _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", *inc, "-c",
-              os.path.join(CSRC, "attn_api.cpp"), "-o", api_o], verbose)
         objs = []
+        for src in HOST_SOURCES:
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", *inc, "-c",
+                  os.path.join(CSRC, src), "-o", obj], verbose)
+            objs.append(obj)
         for src in DEVICE_SOURCES:
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
             _run([hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", *DEVICE_FLAGS,
                   *extra_device_flags, *inc, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
             objs.append(obj)
         tmp_out = output + ".tmp"
-        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_out, *objs, api_o],
-             verbose)
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_out, *objs], verbose)
         os.replace(tmp_out, output)
     return output
 

@@ -209,3 +209,40 @@ def probe_index_inputs(cu, hq, hkv, d, sign, cu_k=None):
     for g in range(hkv):
         v[:, g, 15 + g] = 1.0
     return q, k, v
+
+
+# ---------------------------------------------------------------------------
+# Gated delta rule (the recurrent layers of the paper's hybrid backbone:
+# abstract, result (i); gist.science summary, Metodologia).  The pages give
+# the layer type and the 2k/10k-token prefill, not its head count or sizes;
+# these shapes (16 heads of 128 key and value dims) are a plain choice for a
+# 0.8B-parameter backbone.
+# ---------------------------------------------------------------------------
+
+def make_gdn_inputs(lens, n_heads, dk, dv, seed, decay=(0.85, 1.0)):
+    """(q, k, v, g, beta) for a packed batch of sequences of ``lens`` tokens.
+
+    q and k rows are unit-norm directions (the layer normalises them before
+    the recurrence) rounded to bf16; v ~ N(0, 1) rounded to bf16; the decay
+    alpha ~ U(decay) enters as g = log(alpha) and beta ~ U(0, 1), both
+    rounded to fp32.  Draw order from ``Generator(PCG64(seed))``: q, k, v,
+    alpha, beta, each C-order over its full shape.
+    """
+    T = int(np.sum(lens))
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((T, n_heads, dk))
+    k = rng.standard_normal((T, n_heads, dk))
+    v = rng.standard_normal((T, n_heads, dv))
+    alpha = rng.uniform(decay[0], decay[1], (T, n_heads))
+    beta = rng.uniform(0.0, 1.0, (T, n_heads))
+    q = round_to(q / np.linalg.norm(q, axis=-1, keepdims=True), BF16)
+    k = round_to(k / np.linalg.norm(k, axis=-1, keepdims=True), BF16)
+    return (q, k, round_to(v, BF16), round_to(np.log(alpha), F32), round_to(beta, F32))
+
+
+GDN_WORKLOADS = {
+    # the 10k-token prefill of the paper's long-context case
+    "gdn10k": dict(lens=[10240], n_heads=16, dk=128, dv=128, seed=21),
+    # the packed 4-sequence batch of the attention workloads
+    "gdn_packed": dict(lens=[2048, 5120, 8192, 10240], n_heads=16, dk=128, dv=128, seed=22),
+}
