@@ -27,8 +27,10 @@
 //             its 32 x 128 slice of S in fp32 MFMA accumulators through the
 //             sequence's chunks in order; per chunk U' = U - W S^T and
 //             Q S^T (MFMA), O = diag(scale Gam) Q S^T + P U' (MFMA), then
-//             S <- Gam_last S + Kd U' (MFMA).  The next chunk's workspace
-//             rows are loaded into registers while the current one computes.
+//             S <- Gam_last S + Kd U' (MFMA).  Workspace rows of the chunk
+//             after next load into registers while the current one computes;
+//             the four slices of a (sequence, head) run on one XCD.  Eight
+//             waves split the chunk step by role (see gdn_scan).
 //
 // MFMA operands are bf16 (the state is rounded to bf16 for each product and
 // kept in fp32 between chunks); accumulation is fp32.
@@ -52,8 +54,7 @@ constexpr int DK = kDk;
 constexpr int DV = kDv;
 constexpr int RB = DK + 8;  // bf16 row stride of [*][128] LDS tiles (272 bytes: 17 16-byte slots)
 constexpr int RT = C + 8;   // bf16 row stride of [*][64] LDS tiles (144 bytes: 9 slots)
-constexpr int RF = C + 1;   // fp32 row stride of the 64 x 64 systems
-constexpr int RU = kSliceRows + 8;  // bf16 row stride of a chunk's U slice [64][32]
+constexpr int RU = kSliceRows + 8;  // bf16 row stride of a [*][32] staging tile
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -69,18 +70,39 @@ __device__ __forceinline__ int seq_of_chunk(const GdnArgs &a, int cg) {
   return b;
 }
 
-__global__ __launch_bounds__(256, 1) void gdn_prep(const GdnArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 kl[C * RB];
-  __shared__ __attribute__((aligned(16))) __bf16 ql[C * RB];   // Q; later K^T diag(Gam_last/Gam)
-  __shared__ __attribute__((aligned(16))) __bf16 vl[C * RB];
-  __shared__ float af[C * RF];
-  __shared__ float tf[C * RF];
-  __shared__ float xf[3 * 16 * 17];
-  __shared__ __attribute__((aligned(16))) __bf16 tb[C * RT];
-  __shared__ __attribute__((aligned(16))) __bf16 kts[DK * RT];  // (diag(beta Gam) K)^T
-  __shared__ __attribute__((aligned(16))) __bf16 vts[DV * RT];  // (diag(beta) V)^T
-  __shared__ float gam_s[C], beta_s[C], big_s[C];
-  __bf16 *kdl = ql;  // Q is read only by the score products: its tile then holds [128][64]
+// LDS of gdn_prep, one byte array in four regions reused across phases:
+//   R0  K rows [64][RB] bf16                         (whole kernel)
+//   R1  V rows [64][RB] bf16                         (whole kernel)
+//   R2  Q rows [64][RB] bf16  -> T [64][RF4] fp32     (scores, then the inverse)
+//   R3  A [64][RF4] fp32 + Y                          (the inverse)
+//       -> T diag(beta Gam), T diag(beta) [64][RT] bf16  (the WY products)
+constexpr int RF4 = C + 4;  // fp32 row stride of the 64 x 64 systems (16-byte aligned rows)
+constexpr int kR0 = 0;
+constexpr int kR1 = kR0 + C * RB * 2;
+constexpr int kR2 = kR1 + C * RB * 2;
+constexpr int kR3 = kR2 + C * RB * 2;
+constexpr int kYFloats = 16 * (16 + 32 + 48);  // T_ii A[block i][blocks < i], i = 1..3
+constexpr int kR3Bytes = C * RF4 * 4 + kYFloats * 4;
+constexpr int kPrepLds = kR3 + kR3Bytes;
+static_assert(C * RF4 * 4 <= C * RB * 2, "T fits where Q was");
+static_assert(2 * C * RT * 2 <= kR3Bytes, "both scaled T copies fit where A was");
+static_assert(kPrepLds <= 80 * 1024, "two workgroups per CU");
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kPrepLds];
+  __shared__ float gam_s[C], beta_s[C], big_s[C], fd_s[C];
+  __bf16 *kl = reinterpret_cast<__bf16 *>(lds + kR0);
+  __bf16 *vl = reinterpret_cast<__bf16 *>(lds + kR1);
+  __bf16 *ql = reinterpret_cast<__bf16 *>(lds + kR2);
+  float *tf = reinterpret_cast<float *>(lds + kR2);
+  float *af = reinterpret_cast<float *>(lds + kR3);
+  float *yf = af + C * RF4;
+  __bf16 *tbk = reinterpret_cast<__bf16 *>(lds + kR3);
+  __bf16 *tbv = tbk + C * RT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -120,13 +142,13 @@ __global__ __launch_bounds__(256, 1) void gdn_prep(const GdnArgs a) {
     *reinterpret_cast<bf16x8 *>(ql + r * RB + cc * 8) = qv;
     *reinterpret_cast<bf16x8 *>(vl + r * RB + cc * 8) = vv;
   }
-  for (int idx = tid; idx < C * RF; idx += 256) tf[idx] = 0.0f;
   if (wave == 0) {
-    // inclusive scan of the log-gates over the chunk (padding adds 0)
+    // inclusive scan of the log-gates over the chunk (padding adds 0), kept
+    // in log2 units so every decay below is one exp2
     float x = 0.0f, bt = 0.0f;
     if (lane < n) {
       const size_t th = (size_t)(t0 + lane) * a.h + h;
-      x = a.g[th];
+      x = a.g[th] * kLog2e;
       bt = a.beta[th];
     }
 #pragma unroll
@@ -134,10 +156,12 @@ __global__ __launch_bounds__(256, 1) void gdn_prep(const GdnArgs a) {
       const float y = __shfl_up(x, off);
       if (lane >= off) x += y;
     }
+    const float last = __shfl(x, 63);
     gam_s[lane] = x;
     beta_s[lane] = bt;
-    const float G = expf(x);
+    const float G = exp2_fast(x);
     big_s[lane] = G;
+    fd_s[lane] = exp2_fast(last - x);  // Gam_last / Gam_m <= 1
     gam_out[lane] = G;
   }
   __syncthreads();
@@ -158,139 +182,163 @@ __global__ __launch_bounds__(256, 1) void gdn_prep(const GdnArgs a) {
       }
     }
     const int j = 32 * bj + l32;
+    const float gj = gam_s[j];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int i = 32 * bi + acc_row(e, g);
-      float av = 0.0f, pv = 0.0f;
-      if (i >= j) {
-        const float dec = expf(gam_s[i] - gam_s[j]);  // <= 1: gates are <= 1
-        if (i > j) av = beta_s[i] * dec * kk[e];
-        pv = a.scale * dec * qk[e];
-      }
-      af[i * RF + j] = av;
-      p_out[i * C + j] = (__bf16)pv;
+      const float dec = i >= j ? exp2_fast(gam_s[i] - gj) : 0.0f;  // Gam_i / Gam_j <= 1 for i >= j
+      af[i * RF4 + j] = i > j ? beta_s[i] * dec * kk[e] : 0.0f;
+      p_out[i * C + j] = (__bf16)(a.scale * dec * qk[e]);
     }
   }
-  __syncthreads();
+  __syncthreads();  // Q is no longer read: its region takes T
 
-  // T = (I + A)^-1, A strictly lower.  Diagonal 16 x 16 blocks first: wave w
-  // inverts block w, lane c < 16 computing column c row by row.
+  // T = (I + A)^-1, A strictly lower.  Diagonal 16 x 16 blocks: wave w
+  // inverts block w, lane c < 16 computing column c row by row; the rest of
+  // the lanes clear T above the block diagonal.
   if (lane < 16) {
     const int base = 16 * wave, cc = lane;
     float col[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+      float arow[16];
+#pragma unroll
+      for (int j = 0; j < i; ++j) arow[j] = af[(base + i) * RF4 + base + j];
       float s = (i == cc) ? 1.0f : 0.0f;
 #pragma unroll
-      for (int j = 0; j < i; ++j) s -= af[(base + i) * RF + base + j] * col[j];
+      for (int j = 0; j < i; ++j) s -= arow[j] * col[j];
       col[i] = (i >= cc) ? s : 0.0f;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tf[(base + i) * RF + base + cc] = col[i];
+    for (int i = 0; i < 16; ++i) tf[(base + i) * RF4 + base + cc] = col[i];
+  } else {
+    // rows 16 wave .. +15, columns of the blocks right of the diagonal
+    for (int idx = lane - 16; idx < 16 * (48 - 16 * wave); idx += 48) {
+      const int r = idx / (48 - 16 * wave), cc = 16 * (wave + 1) + idx % (48 - 16 * wave);
+      tf[(16 * wave + r) * RF4 + cc] = 0.0f;
+    }
   }
   __syncthreads();
-  // Off-diagonal blocks by distance d from the diagonal: for i = j + d,
-  //   X = sum_{m in blocks j..i-1} A[i-block][m] T[m][j-block],  T_ij = -T_ii X.
+  // Y_i = T_ii A[block i][columns < 16 i] for i = 1..3 (16 x 16i each), four
+  // columns per task.  Y_i starts at yf + 16 * 8 * i * (i - 1).
+  for (int task = tid; task < 16 * (4 + 8 + 12); task += 256) {
+    const int i = task < 64 ? 1 : (task < 192 ? 2 : 3);
+    const int rel = task - (i == 1 ? 0 : (i == 2 ? 64 : 192));
+    const int r = rel / (4 * i), cq = rel % (4 * i);
+    f32x4 acc = (f32x4)(0.0f);
+    const float *trow = tf + (16 * i + r) * RF4 + 16 * i;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const float t = trow[m];  // T_ii is lower triangular: zero past r
+      acc += t * *reinterpret_cast<const f32x4 *>(af + (16 * i + m) * RF4 + 4 * cq);
+    }
+    *reinterpret_cast<f32x4 *>(yf + 16 * 8 * i * (i - 1) + r * (16 * i) + 4 * cq) = acc;
+  }
+  __syncthreads();
+  // Off-diagonal blocks by distance d: T_ij = -sum_{k in blocks j..i-1} Y_i[r][k] T[k][block j].
   for (int d = 1; d < 4; ++d) {
-    const int nb = 4 - d;
-    for (int o = tid; o < nb * 256; o += 256) {
-      const int bb = o >> 8, r = (o >> 4) & 15, cc = o & 15;
-      const int bj = bb, bi = bb + d;
-      float s = 0.0f;
-      for (int m = 16 * bj; m < 16 * bi; ++m) s += af[(16 * bi + r) * RF + m] * tf[m * RF + 16 * bj + cc];
-      xf[bb * 272 + r * 17 + cc] = s;
-    }
-    __syncthreads();
-    for (int o = tid; o < nb * 256; o += 256) {
-      const int bb = o >> 8, r = (o >> 4) & 15, cc = o & 15;
-      const int bj = bb, bi = bb + d;
-      float s = 0.0f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) s += tf[(16 * bi + r) * RF + 16 * bi + m] * xf[bb * 272 + m * 17 + cc];
-      tf[(16 * bi + r) * RF + 16 * bj + cc] = -s;
+    for (int task = tid; task < (4 - d) * 64; task += 256) {
+      const int bj = task >> 6, bi = bj + d;
+      const int r = (task >> 2) & 15, cq = task & 3;
+      const float *yrow = yf + 16 * 8 * bi * (bi - 1) + r * (16 * bi);
+      f32x4 acc = (f32x4)(0.0f);
+      for (int k = 16 * bj; k < 16 * bi; ++k)
+        acc += yrow[k] * *reinterpret_cast<const f32x4 *>(tf + k * RF4 + 16 * bj + 4 * cq);
+      *reinterpret_cast<f32x4 *>(tf + (16 * bi + r) * RF4 + 16 * bj + 4 * cq) = -acc;
     }
     __syncthreads();
   }
 
-  // bf16 operands: T; (diag(beta Gam) K)^T, (diag(beta) V)^T and
-  // K^T diag(Gam_last / Gam), each transposed to [dim][token].
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int r = idx >> 6, cc = idx & 63;
-    tb[r * RT + cc] = (__bf16)tf[r * RF + cc];
-  }
-  {
-    const float glast = gam_s[C - 1];  // padding repeats the last token's value
-    for (int task = tid; task < (C / 2) * (DK / 8); task += 256) {
-      const int m = 2 * (task >> 4), kc = task & 15;
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8 *>(kl + m * RB + 8 * kc);
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8 *>(kl + (m + 1) * RB + 8 * kc);
-      const bf16x8 v0 = *reinterpret_cast<const bf16x8 *>(vl + m * RB + 8 * kc);
-      const bf16x8 v1 = *reinterpret_cast<const bf16x8 *>(vl + (m + 1) * RB + 8 * kc);
-      const float fk0 = beta_s[m] * big_s[m], fk1 = beta_s[m + 1] * big_s[m + 1];
-      const float fv0 = beta_s[m], fv1 = beta_s[m + 1];
-      const float fd0 = expf(glast - gam_s[m]), fd1 = expf(glast - gam_s[m + 1]);
+  // bf16 T diag(beta Gam) and T diag(beta) (A and Y are no longer needed)
+  for (int idx = tid; idx < C * C / 4; idx += 256) {
+    const int r = idx >> 4, cq = idx & 15;
+    const f32x4 t = *reinterpret_cast<const f32x4 *>(tf + r * RF4 + 4 * cq);
+    bf16x4 xk, xv;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = 8 * kc + e;
-        *reinterpret_cast<bf16x2 *>(kts + row * RT + m) =
-            bf16x2{(__bf16)(fk0 * (float)k0[e]), (__bf16)(fk1 * (float)k1[e])};
-        *reinterpret_cast<bf16x2 *>(vts + row * RT + m) =
-            bf16x2{(__bf16)(fv0 * (float)v0[e]), (__bf16)(fv1 * (float)v1[e])};
-        *reinterpret_cast<bf16x2 *>(kdl + row * C + m) =
-            bf16x2{(__bf16)(fd0 * (float)k0[e]), (__bf16)(fd1 * (float)k1[e])};
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * cq + e;
+      xk[e] = (__bf16)(t[e] * beta_s[m] * big_s[m]);
+      xv[e] = (__bf16)(t[e] * beta_s[m]);
     }
+    *reinterpret_cast<bf16x4 *>(tbk + r * RT + 4 * cq) = xk;
+    *reinterpret_cast<bf16x4 *>(tbv + r * RT + 4 * cq) = xv;
+  }
+  // K^T diag(Gam_last / Gam) to the workspace: eight tokens of one key dim per task
+  for (int task = tid; task < DK * (C / 8); task += 256) {
+    const int k = task >> 3, m0 = 8 * (task & 7);
+    bf16x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (__bf16)(fd_s[m0 + e] * (float)kl[(m0 + e) * RB + k]);
+    *reinterpret_cast<bf16x8 *>(kd_out + k * C + m0) = x;
   }
   __syncthreads();
 
-  // K^T diag(Gam_last / Gam) to the workspace, 16 bytes at a time
-  for (int idx = tid; idx < DK * (C / 8); idx += 256) {
-    const int r = idx >> 3, cc = idx & 7;
-    *reinterpret_cast<bf16x8 *>(kd_out + r * C + cc * 8) = *reinterpret_cast<const bf16x8 *>(kdl + r * C + cc * 8);
-  }
-  // W = T (diag(beta Gam) K), U = T (diag(beta) V): wave w -> columns
-  // 32w .. 32w+31 of both, all 64 rows (two 32-row blocks).
+  // W = (T diag(beta Gam)) K, U = (T diag(beta)) V: wave w -> columns
+  // 32w .. 32w+31 of both, all 64 rows; K and V are read down their columns.
   {
     f32x16 wacc[2] = {(f32x16)(0.0f), (f32x16)(0.0f)};
     f32x16 uacc[2] = {(f32x16)(0.0f), (f32x16)(0.0f)};
+    const int col = 32 * wave + l32;
 #pragma unroll
     for (int ks = 0; ks < C / 16; ++ks) {
-      const bf16x8 bw = *reinterpret_cast<const bf16x8 *>(kts + (32 * wave + l32) * RT + 16 * ks + 8 * g);
-      const bf16x8 bu = *reinterpret_cast<const bf16x8 *>(vts + (32 * wave + l32) * RT + 16 * ks + 8 * g);
+      bf16x8 bw, bu;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bw[e] = kl[(16 * ks + 8 * g + e) * RB + col];
+        bu[e] = vl[(16 * ks + 8 * g + e) * RB + col];
+      }
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
-        const bf16x8 at = *reinterpret_cast<const bf16x8 *>(tb + (32 * ib + l32) * RT + 16 * ks + 8 * g);
-        wacc[ib] = mfma(at, bw, wacc[ib]);
-        uacc[ib] = mfma(at, bu, uacc[ib]);
+        wacc[ib] = mfma(*reinterpret_cast<const bf16x8 *>(tbk + (32 * ib + l32) * RT + 16 * ks + 8 * g), bw, wacc[ib]);
+        uacc[ib] = mfma(*reinterpret_cast<const bf16x8 *>(tbv + (32 * ib + l32) * RT + 16 * ks + 8 * g), bu, uacc[ib]);
       }
     }
-    const int col = 32 * wave + l32;
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int i = 32 * ib + acc_row(e, g);
-        w_out[i * DK + col] = (__bf16)wacc[ib][e];
-        u_out[i * DV + col] = (__bf16)uacc[ib][e];
+      for (int e = 0; e < 16; ++e) w_out[(32 * ib + acc_row(e, g)) * DK + col] = (__bf16)wacc[ib][e];
+    // U transposed, [v][t]: four consecutive tokens per store
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (__bf16)uacc[ib][4 * q4 + e];
+        *reinterpret_cast<bf16x4 *>(u_out + col * C + 32 * ib + 8 * q4 + 4 * g) = x;
       }
   }
 }
 
-// Registers holding one chunk's workspace rows and queries on their way to LDS.
+// Registers holding one chunk's workspace rows and queries on their way to
+// LDS (the four state waves of gdn_scan load them, 256 threads).
 struct ChunkRegs {
   bf16x8 w[4], q[4], kd[4], p[2], u;
   float gam;
 };
 
-__global__ __launch_bounds__(256, 1) void gdn_scan(const GdnArgs a) {
+// Eight waves per workgroup (two per SIMD, so one hides the other's
+// latencies), each with one role per chunk:
+//   waves 0, 1  X = W S^T for token block 32w .. (8 MFMAs), then U' = U - X;
+//               the chain the next chunk depends on
+//   waves 2, 3  Y = Q S^T for token block 32(w-2) .., then after U' is
+//               ready O = diag(scale Gam) Y + P U' and the output store
+//   waves 4..7  after U' is ready S^T[32(w-4) ..] <- Gam_last S^T + Kd U';
+//               they also issue every load of the chunk after next and move
+//               the next chunk from registers into the other LDS buffer, so
+//               load issue never stalls waves 0..3.
+constexpr int kScanWaves = 8;
+
+__global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 wl[2][C * RB];
   __shared__ __attribute__((aligned(16))) __bf16 qsl[2][C * RB];
   __shared__ __attribute__((aligned(16))) __bf16 pl[2][C * RT];
   __shared__ __attribute__((aligned(16))) __bf16 kdl[2][DK * RT];
-  __shared__ __attribute__((aligned(16))) __bf16 ul[2][C * RU];
-  __shared__ float gl[2][C];
-  __shared__ __attribute__((aligned(16))) __bf16 sb[kSliceRows * RB];   // S rows [v][k], bf16
-  __shared__ __attribute__((aligned(16))) __bf16 upt[kSliceRows * RT];  // U'^T [v][t], bf16
+  __shared__ __attribute__((aligned(16))) __bf16 ul[2][kSliceRows * RT];  // U^T rows [v][t]
+  __shared__ __attribute__((aligned(16))) float gl[2][C];
+  __shared__ __attribute__((aligned(16))) __bf16 sb[kSliceRows * RB];     // S rows [v][k], bf16
+  __shared__ __attribute__((aligned(16))) __bf16 upt[kSliceRows * RT];    // U'^T rows [v][t], bf16
+  __shared__ __attribute__((aligned(16))) __bf16 ost[2][32 * RU];         // output rows [t][v]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -298,23 +346,36 @@ __global__ __launch_bounds__(256, 1) void gdn_scan(const GdnArgs a) {
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
+  // Workgroup -> (pair = sequence x head, slice of 32 value dims).
+  // Consecutive workgroups go to the eight XCDs in turn, so the four slices
+  // of a pair are placed eight apart: they run on one XCD and share the
+  // chunk rows in its L2.
   constexpr int SLICES = DV / kSliceRows;
-  const int s = blockIdx.x % SLICES;
-  const int bh = blockIdx.x / SLICES;
-  const int h = bh % a.h;
-  const int b = bh / a.h;
+  const int xcd = blockIdx.x & 7;
+  const int j8 = blockIdx.x >> 3;
+  const int pair = xcd + 8 * (j8 / SLICES);
+  const int s = j8 % SLICES;
+  if (pair >= a.n_seqs * a.h) return;  // grid padding; whole workgroup, before any barrier
+  const int h = pair % a.h;
+  const int b = pair / a.h;
   const int nchunks = a.chunk_start[b + 1] - a.chunk_start[b];
   const int seq_len = a.seq_len[b];
   const int seq0 = a.seq_start[b];
+  const int v0 = kSliceRows * s;
   const size_t state_off = ((size_t)(a.seq_base + b) * a.h + h) * DV * DK;
 
-  // State slice S^T[k][v], k = 32 wave + acc_row, v = 32 s + l32.
+  const bool x_wave = wave < 2, y_wave = wave >= 2 && wave < 4, s_wave = wave >= 4;
+  const int tb = 32 * (wave & 1);   // token block of X / Y / O
+  const int kb = 32 * (wave - 4);   // key rows of the state (state waves)
+  const int ltid = tid - 256;       // thread index among the state waves
+
+  // State waves: S^T[kb + row][v0 + l32].
   f32x16 st = (f32x16)(0.0f);
-  if (a.s0 != nullptr) {
+  if (s_wave && a.s0 != nullptr) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 x = *reinterpret_cast<const f32x4 *>(a.s0 + state_off + (size_t)(32 * s + l32) * DK +
-                                                       32 * wave + 8 * q4 + 4 * g);
+      const f32x4 x = *reinterpret_cast<const f32x4 *>(a.s0 + state_off + (size_t)(v0 + l32) * DK + kb +
+                                                       8 * q4 + 4 * g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) st[4 * q4 + e] = x[e];
     }
@@ -331,26 +392,26 @@ __global__ __launch_bounds__(256, 1) void gdn_scan(const GdnArgs a) {
     const int n = min(C, seq_len - c * C);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
+      const int idx = ltid + 256 * i;
       const int row = idx >> 4, cc = idx & 15;
       r.w[i] = *reinterpret_cast<const bf16x8 *>(w + row * DK + cc * 8);
-      r.q[i] = row < n ? *reinterpret_cast<const bf16x8 *>(Q + ((size_t)(t0 + row) * a.h + h) * DK + cc * 8)
-                       : (bf16x8)((__bf16)0.0f);
-      const int krow = idx >> 3, kc = idx & 7;
-      r.kd[i] = *reinterpret_cast<const bf16x8 *>(kd + krow * C + kc * 8);
+      // rows past the chunk repeat its last token: they only feed output
+      // rows that are never stored (no select, so nothing waits on the load)
+      r.q[i] = *reinterpret_cast<const bf16x8 *>(Q + ((size_t)(t0 + min(row, n - 1)) * a.h + h) * DK + cc * 8);
+      r.kd[i] = *reinterpret_cast<const bf16x8 *>(kd + (idx >> 3) * C + (idx & 7) * 8);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 256 * i;
+      const int idx = ltid + 256 * i;
       r.p[i] = *reinterpret_cast<const bf16x8 *>(p + (idx >> 3) * C + (idx & 7) * 8);
     }
-    r.u = *reinterpret_cast<const bf16x8 *>(u + (tid >> 2) * DV + kSliceRows * s + (tid & 3) * 8);
-    r.gam = tid < C ? a.ws_gam[item * C + tid] : 0.0f;
+    r.u = *reinterpret_cast<const bf16x8 *>(u + (v0 + (ltid >> 3)) * C + (ltid & 7) * 8);
+    r.gam = a.ws_gam[item * C + (ltid & (C - 1))];
   };
   auto store_chunk = [&](int buf, const ChunkRegs &r) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i;
+      const int idx = ltid + 256 * i;
       const int row = idx >> 4, cc = idx & 15;
       *reinterpret_cast<bf16x8 *>(&wl[buf][row * RB + cc * 8]) = r.w[i];
       *reinterpret_cast<bf16x8 *>(&qsl[buf][row * RB + cc * 8]) = r.q[i];
@@ -358,101 +419,130 @@ __global__ __launch_bounds__(256, 1) void gdn_scan(const GdnArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 256 * i;
+      const int idx = ltid + 256 * i;
       *reinterpret_cast<bf16x8 *>(&pl[buf][(idx >> 3) * RT + (idx & 7) * 8]) = r.p[i];
     }
-    *reinterpret_cast<bf16x8 *>(&ul[buf][(tid >> 2) * RU + (tid & 3) * 8]) = r.u;
-    if (tid < C) gl[buf][tid] = r.gam;
+    *reinterpret_cast<bf16x8 *>(&ul[buf][(ltid >> 3) * RT + (ltid & 7) * 8]) = r.u;
+    if (ltid < C) gl[buf][ltid] = r.gam;
   };
-  // bf16 copy of the state slice as S rows [v][k] (B operand of W S^T, Q S^T)
+  // state waves: bf16 copy of the state as S rows [v][k]
   auto store_state = [&]() {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       bf16x4 x;
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = (__bf16)st[4 * q4 + e];
-      *reinterpret_cast<bf16x4 *>(&sb[l32 * RB + 32 * wave + 8 * q4 + 4 * g]) = x;
+      *reinterpret_cast<bf16x4 *>(&sb[l32 * RB + kb + 8 * q4 + 4 * g]) = x;
     }
   };
 
-  ChunkRegs nxt;
-  if (nchunks > 0) {
-    load_chunk(0, nxt);
-    store_chunk(0, nxt);
-  }
-  store_state();
-  __syncthreads();
-
-  for (int c = 0; c < nchunks; ++c) {
+  // One chunk step: chunk c computes from LDS buffer c & 1; the state waves
+  // hold chunk c + 1 in `ahead`, load chunk c + 2 into `fill` and, once
+  // chunk c - 1's readers are long past (they finished before this step's
+  // first barrier), write chunk c + 1 into the other buffer.
+  auto step = [&](int c, ChunkRegs &ahead, ChunkRegs &fill) __attribute__((always_inline)) {
     const int buf = c & 1;
-    if (c + 1 < nchunks) load_chunk(c + 1, nxt);
     const int t0 = seq0 + c * C;
     const int n = min(C, seq_len - c * C);
-
-    // waves 0, 1: X = W S^T (token rows 32 wave ..); waves 2, 3: Y = Q S^T
-    const int tb = 32 * (wave & 1);
-    const __bf16 *arow = (wave < 2 ? wl[buf] : qsl[buf]) + (tb + l32) * RB + 8 * g;
     f32x16 xy = (f32x16)(0.0f);
+    if (s_wave) {
+      // unconditional (past the end: the last chunk again, never used), so
+      // the compiler counts the loads in flight exactly
+      load_chunk(min(c + 2, nchunks - 1), fill);
+    } else {
+      // X = W S^T (waves 0, 1) or Y = Q S^T (waves 2, 3) for token block tb
+      const __bf16 *arow = (x_wave ? wl[buf] : qsl[buf]) + (tb + l32) * RB + 8 * g;
+      bf16x8 av[DK / 16], bv[DK / 16];
 #pragma unroll
-    for (int ks = 0; ks < DK / 16; ++ks) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8 *>(arow + 16 * ks);
-      const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(&sb[l32 * RB + 16 * ks + 8 * g]);
-      xy = mfma(av, bv, xy);
-    }
-    if (wave < 2) {
-      // U' = U - X, stored transposed [v][t] in bf16
+      for (int ks = 0; ks < DK / 16; ++ks) {
+        av[ks] = *reinterpret_cast<const bf16x8 *>(arow + 16 * ks);
+        bv[ks] = *reinterpret_cast<const bf16x8 *>(&sb[l32 * RB + 16 * ks + 8 * g]);
+      }
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        bf16x4 x;
+      for (int ks = 0; ks < DK / 16; ++ks) xy = mfma(av[ks], bv[ks], xy);
+      if (x_wave) {
+        // U' = U - X, stored transposed [v][t] in bf16
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = tb + 8 * q4 + 4 * g + e;
-          x[e] = (__bf16)((float)ul[buf][t * RU + l32] - xy[4 * q4 + e]);
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int t = tb + 8 * q4 + 4 * g;
+          const bf16x4 u4 = *reinterpret_cast<const bf16x4 *>(&ul[buf][l32 * RT + t]);
+          bf16x4 up;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) up[e] = (__bf16)((float)u4[e] - xy[4 * q4 + e]);
+          *reinterpret_cast<bf16x4 *>(&upt[l32 * RT + t]) = up;
         }
-        *reinterpret_cast<bf16x4 *>(&upt[l32 * RT + tb + 8 * q4 + 4 * g]) = x;
       }
     }
-    __syncthreads();
+    __syncthreads();  // U' ready; every read of sb done
 
-    if (wave >= 2) {
+    if (y_wave) {
       // O = diag(scale Gam) Q S^T + P U'
 #pragma unroll
-      for (int e = 0; e < 16; ++e) xy[e] *= a.scale * gl[buf][tb + acc_row(e, g)];
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 gm = *reinterpret_cast<const f32x4 *>(&gl[buf][tb + 8 * q4 + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xy[4 * q4 + e] *= a.scale * gm[e];
+      }
+      bf16x8 ap[C / 16], bu[C / 16];
 #pragma unroll
       for (int ks = 0; ks < C / 16; ++ks) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8 *>(&pl[buf][(tb + l32) * RT + 16 * ks + 8 * g]);
-        const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(&upt[l32 * RT + 16 * ks + 8 * g]);
-        xy = mfma(av, bv, xy);
+        ap[ks] = *reinterpret_cast<const bf16x8 *>(&pl[buf][(tb + l32) * RT + 16 * ks + 8 * g]);
+        bu[ks] = *reinterpret_cast<const bf16x8 *>(&upt[l32 * RT + 16 * ks + 8 * g]);
       }
+#pragma unroll
+      for (int ks = 0; ks < C / 16; ++ks) xy = mfma(ap[ks], bu[ks], xy);
+      // through this wave's LDS tile to 16-byte row stores
+      __bf16 *os = ost[wave - 2];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) os[acc_row(e, g) * RU + l32] = (__bf16)xy[e];
       __bf16 *orow = reinterpret_cast<__bf16 *>(a.out);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int t = tb + acc_row(e, g);
-        if (t < n) orow[((size_t)(t0 + t) * a.h + h) * DV + kSliceRows * s + l32] = (__bf16)xy[e];
+      for (int i = 0; i < 2; ++i) {
+        const int j = lane + 64 * i;
+        const int t = j >> 2, cq = j & 3;
+        const bf16x8 ov = *reinterpret_cast<const bf16x8 *>(os + t * RU + 8 * cq);
+        if (tb + t < n)
+          *reinterpret_cast<bf16x8 *>(orow + ((size_t)(t0 + tb + t) * a.h + h) * DV + v0 + 8 * cq) = ov;
       }
-    }
-    // S^T <- Gam_last S^T + Kd U'
-    const float glast = gl[buf][C - 1];
+    } else if (s_wave) {
+      // S^T <- Gam_last S^T + Kd U'
+      const float glast = gl[buf][C - 1];
+      bf16x8 ak[C / 16], bu[C / 16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) st[e] *= glast;
+      for (int ks = 0; ks < C / 16; ++ks) {
+        ak[ks] = *reinterpret_cast<const bf16x8 *>(&kdl[buf][(kb + l32) * RT + 16 * ks + 8 * g]);
+        bu[ks] = *reinterpret_cast<const bf16x8 *>(&upt[l32 * RT + 16 * ks + 8 * g]);
+      }
 #pragma unroll
-    for (int ks = 0; ks < C / 16; ++ks) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8 *>(&kdl[buf][(32 * wave + l32) * RT + 16 * ks + 8 * g]);
-      const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(&upt[l32 * RT + 16 * ks + 8 * g]);
-      st = mfma(av, bv, st);
+      for (int e = 0; e < 16; ++e) st[e] *= glast;
+#pragma unroll
+      for (int ks = 0; ks < C / 16; ++ks) st = mfma(ak[ks], bu[ks], st);
+      store_state();
+      store_chunk(buf ^ 1, ahead);  // past the end: a copy nobody reads
     }
-    store_state();
-    if (c + 1 < nchunks) store_chunk(buf ^ 1, nxt);
-    __syncthreads();
+    __syncthreads();  // next chunk's rows and the new state ready
+  };
+
+  ChunkRegs ra, rb;
+  if (s_wave && nchunks > 0) {
+    load_chunk(0, ra);
+    store_chunk(0, ra);
+    load_chunk(min(1, nchunks - 1), rb);
+  }
+  if (s_wave) store_state();
+  __syncthreads();
+  for (int c = 0; c < nchunks; c += 2) {
+    step(c, rb, ra);
+    if (c + 1 < nchunks) step(c + 1, ra, rb);
   }
 
-  if (a.s_final != nullptr) {
+  if (s_wave && a.s_final != nullptr) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       f32x4 x;
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = st[4 * q4 + e];
-      *reinterpret_cast<f32x4 *>(a.s_final + state_off + (size_t)(32 * s + l32) * DK + 32 * wave + 8 * q4 + 4 * g) = x;
+      *reinterpret_cast<f32x4 *>(a.s_final + state_off + (size_t)(v0 + l32) * DK + kb + 8 * q4 + 4 * g) = x;
     }
   }
 }
@@ -466,8 +556,10 @@ int launch_gdn(const GdnArgs &a, void *stream) {
   if (a.total_items > 0)
     e = hipLaunchKernel(reinterpret_cast<const void *>(gdn_prep), dim3(a.total_items), dim3(256), args, 0, st);
   if (e == hipSuccess && a.n_seqs > 0)
-    e = hipLaunchKernel(reinterpret_cast<const void *>(gdn_scan), dim3(a.n_seqs * a.h * (kDv / kSliceRows)),
-                        dim3(256), args, 0, st);
+    // pairs rounded up to a multiple of 8 (see gdn_scan's workgroup map)
+    e = hipLaunchKernel(reinterpret_cast<const void *>(gdn_scan),
+                        dim3((a.n_seqs * a.h + 7) / 8 * 8 * (kDv / kSliceRows)), dim3(kScanWaves * 64), args, 0,
+                        st);
   return static_cast<int>(e);
 }
 

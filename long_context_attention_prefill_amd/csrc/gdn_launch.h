@@ -13,11 +13,11 @@ constexpr int kChunk = 64;              // tokens per chunk
 constexpr int kMaxSeqsPerLaunch = 64;   // longer batches: several launches in order
 constexpr int kDk = 128;
 constexpr int kDv = 128;
-constexpr int kSliceRows = 32;          // state rows (value dims) per scan workgroup
+constexpr int kSliceRows = 32;          // value dims per MFMA block of the state (a scan workgroup takes two)
 
 // Workspace per (chunk, head) item, each array item-major:
 //   w    bf16 [64][128]  T diag(beta Gamma) K       (WY key combinations)
-//   u    bf16 [64][128]  T diag(beta) V             (WY value combinations)
+//   u    bf16 [128][64]  (T diag(beta) V)^T         (WY value combinations, transposed)
 //   p    bf16 [64][64]   scale (Q K^T o M), M_ij = Gamma_i / Gamma_j (i >= j)
 //   kd   bf16 [128][64]  K^T diag(Gamma_last / Gamma)  (transposed)
 //   gam  f32  [64]       Gamma_i = exp(cumulative g within the chunk)
