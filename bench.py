@@ -9,10 +9,11 @@ shape: causal 2048 tokens (16/16 heads), and the packed 4-sequence batch
 (2048 + 5120 + 8192 + 10240 tokens, 16/2 heads) under the causal and the
 256-token window mask; the 10k sequence prefilled in five 2048-query chunks
 over its growing cache (attn_prefill_kv); and decode (attn_decode) of one
-and of 64 newest tokens over 10240-token caches.  Each of these is timed as
->= 20 samples of R back-to-back calls (R chosen so a sample lasts >= 1 ms)
-between two events, reported per call as median / min / p90.  Prints ONE
-JSON line.
+and of 64 newest tokens over 10240-token caches; the chunked gated delta rule
+(gdn_prefill) over the 10k sequence and the packed batch, 16 heads of 128.
+Each of these is timed as >= 20 samples of R back-to-back calls (R chosen so
+a sample lasts >= 1 ms) between two events, reported per call as median /
+min / p90.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only]
                     [--no-cpu-baseline] [--sweep] [--copy-calibration]
@@ -218,6 +219,43 @@ def decode_step(n_seqs, cache_len, hq, hkv, d=128, seed=0):
             "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
 
 
+def gdn_step(name):
+    """gdn_prefill (chunked gated delta rule) on one of the seeded workloads:
+    time per call and the HBM rate of its algorithmic bytes (q, k, v read and
+    out written in bf16, g and beta read in fp32, final states written)."""
+    import torch
+
+    import long_context_attention_prefill_amd as lcap
+    from long_context_attention_prefill_amd import workloads as W
+
+    spec = W.GDN_WORKLOADS[name]
+    lens, H, dk, dv = spec["lens"], spec["n_heads"], spec["dk"], spec["dv"]
+    q, k, v, g, beta = W.make_gdn_inputs(lens, H, dk, dv, spec["seed"])
+    cu = [0] + [int(x) for x in np.cumsum(lens)]
+    dev = [torch.from_numpy(x).to(torch.bfloat16).to("cuda") for x in (q, k, v)]
+    gd, bd = (torch.from_numpy(x).to(torch.float32).to("cuda") for x in (g, beta))
+    ws = torch.empty(max(lcap.gdn_prefill_workspace_size(cu, H, dk, dv), 16), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(dev[2])
+    fin = torch.empty((len(lens), H, dv, dk), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(dk)
+    per_call, reps = event_samples(lambda: lcap.gdn_prefill(
+        dev[0], dev[1], dev[2], gd, bd, cu, scale=scale, out=out, final_state=fin, workspace=ws))
+    med = float(np.median(per_call))
+    T = cu[-1]
+    byts = T * H * (2 * dk + 2 * dv) * 2 + T * H * 8 + len(lens) * H * dv * dk * 4
+    gbs = byts / (med * 1e-3) / 1e9
+    del dev, gd, bd, ws, out, fin
+    return {"workload": f"gated delta rule prefill, {'+'.join(str(x) for x in lens)} tokens, {H} "
+                        f"heads, d_k {dk} / d_v {dv}, bf16, chunks of 64",
+            "ms_median": round(med, 5), "ms_min": round(float(per_call.min()), 5),
+            "ms_p90": round(float(np.percentile(per_call, 90)), 5),
+            "samples": int(per_call.size), "calls_per_sample": reps,
+            "tokens_per_s": round(T / (med * 1e-3), 1),
+            "algorithmic_bytes": byts, "algorithmic_hbm_gbs": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
+
+
 def gpu_clock():
     """Current shader clock as rocm-smi reports it (best effort, text)."""
     import subprocess
@@ -355,6 +393,9 @@ def main():
         others["decode_1"] = decode_step(1, 10240, 16, 2)
         others["decode_64"] = decode_step(64, 10240, 16, 2)
         torch.cuda.empty_cache()
+        others["gdn10k"] = gdn_step("gdn10k")
+        others["gdn_packed"] = gdn_step("gdn_packed")
+        torch.cuda.empty_cache()
 
     sweep = None
     if args.sweep:
@@ -407,6 +448,8 @@ def main():
         line["chunked_prefill_10k"] = others["chunked"]
         line["decode_10k_cache_b1"] = others["decode_1"]
         line["decode_10k_cache_b64"] = others["decode_64"]
+        line["gated_delta_rule_10k"] = others["gdn10k"]
+        line["gated_delta_rule_packed"] = others["gdn_packed"]
         line["gpu_clock"] = gpu_clock()
     if sweep is not None:
         line["sweep_tflops_16x2_causal"] = sweep

@@ -310,10 +310,10 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
   }
 }
 
-// Registers holding one chunk's workspace rows and queries on their way to
-// LDS (the four state waves of gdn_scan load them, 256 threads).
+// Registers holding a thread's share of one chunk's workspace rows and
+// queries on their way to LDS (all 512 threads of gdn_scan take part).
 struct ChunkRegs {
-  bf16x8 w[4], q[4], kd[4], p[2], u;
+  bf16x8 w[2], q[2], kd[2], p, u;
   float gam;
 };
 
@@ -323,10 +323,10 @@ struct ChunkRegs {
 //               the chain the next chunk depends on
 //   waves 2, 3  Y = Q S^T for token block 32(w-2) .., then after U' is
 //               ready O = diag(scale Gam) Y + P U' and the output store
-//   waves 4..7  after U' is ready S^T[32(w-4) ..] <- Gam_last S^T + Kd U';
-//               they also issue every load of the chunk after next and move
-//               the next chunk from registers into the other LDS buffer, so
-//               load issue never stalls waves 0..3.
+//   waves 4..7  after U' is ready S^T[32(w-4) ..] <- Gam_last S^T + Kd U'.
+// Every wave also moves its share of the next chunk from registers into the
+// other LDS buffer and loads its share of the chunk after next, at the point
+// of the step where that costs its role least (waves 0, 1 after U').
 constexpr int kScanWaves = 8;
 
 __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) {
@@ -367,7 +367,6 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
   const bool x_wave = wave < 2, y_wave = wave >= 2 && wave < 4, s_wave = wave >= 4;
   const int tb = 32 * (wave & 1);   // token block of X / Y / O
   const int kb = 32 * (wave - 4);   // key rows of the state (state waves)
-  const int ltid = tid - 256;       // thread index among the state waves
 
   // State waves: S^T[kb + row][v0 + l32].
   f32x16 st = (f32x16)(0.0f);
@@ -391,8 +390,8 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
     const int t0 = seq0 + c * C;
     const int n = min(C, seq_len - c * C);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = ltid + 256 * i;
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 512 * i;
       const int row = idx >> 4, cc = idx & 15;
       r.w[i] = *reinterpret_cast<const bf16x8 *>(w + row * DK + cc * 8);
       // rows past the chunk repeat its last token: they only feed output
@@ -400,30 +399,23 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
       r.q[i] = *reinterpret_cast<const bf16x8 *>(Q + ((size_t)(t0 + min(row, n - 1)) * a.h + h) * DK + cc * 8);
       r.kd[i] = *reinterpret_cast<const bf16x8 *>(kd + (idx >> 3) * C + (idx & 7) * 8);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = ltid + 256 * i;
-      r.p[i] = *reinterpret_cast<const bf16x8 *>(p + (idx >> 3) * C + (idx & 7) * 8);
-    }
-    r.u = *reinterpret_cast<const bf16x8 *>(u + (v0 + (ltid >> 3)) * C + (ltid & 7) * 8);
-    r.gam = a.ws_gam[item * C + (ltid & (C - 1))];
+    r.p = *reinterpret_cast<const bf16x8 *>(p + (tid >> 3) * C + (tid & 7) * 8);
+    // the U slice is 256 pieces: both halves of the workgroup load it
+    r.u = *reinterpret_cast<const bf16x8 *>(u + (v0 + ((tid & 255) >> 3)) * C + (tid & 7) * 8);
+    r.gam = a.ws_gam[item * C + (tid & (C - 1))];
   };
   auto store_chunk = [&](int buf, const ChunkRegs &r) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = ltid + 256 * i;
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 512 * i;
       const int row = idx >> 4, cc = idx & 15;
       *reinterpret_cast<bf16x8 *>(&wl[buf][row * RB + cc * 8]) = r.w[i];
       *reinterpret_cast<bf16x8 *>(&qsl[buf][row * RB + cc * 8]) = r.q[i];
       *reinterpret_cast<bf16x8 *>(&kdl[buf][(idx >> 3) * RT + (idx & 7) * 8]) = r.kd[i];
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = ltid + 256 * i;
-      *reinterpret_cast<bf16x8 *>(&pl[buf][(idx >> 3) * RT + (idx & 7) * 8]) = r.p[i];
-    }
-    *reinterpret_cast<bf16x8 *>(&ul[buf][(ltid >> 3) * RT + (ltid & 7) * 8]) = r.u;
-    if (ltid < C) gl[buf][ltid] = r.gam;
+    *reinterpret_cast<bf16x8 *>(&pl[buf][(tid >> 3) * RT + (tid & 7) * 8]) = r.p;
+    if (tid < 256) *reinterpret_cast<bf16x8 *>(&ul[buf][(tid >> 3) * RT + (tid & 7) * 8]) = r.u;
+    if (tid < C) gl[buf][tid] = r.gam;
   };
   // state waves: bf16 copy of the state as S rows [v][k]
   auto store_state = [&]() {
@@ -436,19 +428,21 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
     }
   };
 
-  // One chunk step: chunk c computes from LDS buffer c & 1; the state waves
-  // hold chunk c + 1 in `ahead`, load chunk c + 2 into `fill` and, once
-  // chunk c - 1's readers are long past (they finished before this step's
-  // first barrier), write chunk c + 1 into the other buffer.
+  // One chunk step: chunk c computes from LDS buffer c & 1 while every wave
+  // writes its share of chunk c + 1 (held in `ahead`) into the other buffer
+  // (its last readers, chunk c - 1's, finished before this step began) and
+  // loads its share of chunk c + 2 into `fill` -- unconditionally (past the
+  // end: the last chunk again, never used), so the compiler counts the
+  // loads in flight exactly.
   auto step = [&](int c, ChunkRegs &ahead, ChunkRegs &fill) __attribute__((always_inline)) {
     const int buf = c & 1;
     const int t0 = seq0 + c * C;
     const int n = min(C, seq_len - c * C);
+    const int cn = min(c + 2, nchunks - 1);
     f32x16 xy = (f32x16)(0.0f);
     if (s_wave) {
-      // unconditional (past the end: the last chunk again, never used), so
-      // the compiler counts the loads in flight exactly
-      load_chunk(min(c + 2, nchunks - 1), fill);
+      store_chunk(buf ^ 1, ahead);
+      load_chunk(cn, fill);
     } else {
       // X = W S^T (waves 0, 1) or Y = Q S^T (waves 2, 3) for token block tb
       const __bf16 *arow = (x_wave ? wl[buf] : qsl[buf]) + (tb + l32) * RB + 8 * g;
@@ -472,6 +466,8 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
           *reinterpret_cast<bf16x4 *>(&upt[l32 * RT + t]) = up;
         }
       }
+      store_chunk(buf ^ 1, ahead);
+      load_chunk(cn, fill);
     }
     __syncthreads();  // U' ready; every read of sb done
 
@@ -518,13 +514,12 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
 #pragma unroll
       for (int ks = 0; ks < C / 16; ++ks) st = mfma(ak[ks], bu[ks], st);
       store_state();
-      store_chunk(buf ^ 1, ahead);  // past the end: a copy nobody reads
     }
     __syncthreads();  // next chunk's rows and the new state ready
   };
 
   ChunkRegs ra, rb;
-  if (s_wave && nchunks > 0) {
+  if (nchunks > 0) {
     load_chunk(0, ra);
     store_chunk(0, ra);
     load_chunk(min(1, nchunks - 1), rb);
