@@ -10,8 +10,9 @@ shape: causal 2048 tokens (16/16 heads), and the packed 4-sequence batch
 256-token window mask; the 10k sequence prefilled in five 2048-query chunks
 over its growing cache (attn_prefill_kv); and decode (attn_decode) of one
 and of 64 newest tokens over 10240-token caches; the chunked gated delta rule
-(gdn_prefill) over the 10k sequence and the packed batch, 16 heads of 128.
-Each of these is timed as >= 20 samples of R back-to-back calls (R chosen so
+(gdn_prefill) over the 10k sequence and the packed batch, 16 heads of 128;
+the QKV and output projections of the 10k sequence (int8 weights dequantized
+once, vendor bf16 GEMM).  Each of these is timed as >= 20 samples of R back-to-back calls (R chosen so
 a sample lasts >= 1 ms) between two events, reported per call as median /
 min / p90.  Prints ONE JSON line.
 
@@ -256,6 +257,36 @@ def gdn_step(name):
             "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
 
 
+def proj_step(t, n, k, seed):
+    """Projection around attention: int8 weights [n, k] dequantized once to
+    bf16 (HBM rate of 1 byte read + 2 written per weight), then y = x w^T for
+    t tokens by the vendor GEMM (TFLOP/s against the bf16 MFMA peak)."""
+    import torch
+
+    import long_context_attention_prefill_amd as lcap
+
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    q = torch.randint(-128, 128, (n, k), generator=g, device="cuda", dtype=torch.int8)
+    scale = torch.rand(n, generator=g, device="cuda") / 64.0
+    x = torch.randn(t, k, generator=g, device="cuda").to(torch.bfloat16)
+    w = torch.empty((n, k), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((t, n), dtype=torch.bfloat16, device="cuda")
+    dq, _ = event_samples(lambda: lcap.proj_dequantize_int8(q, scale, out=w))
+    mm, reps = event_samples(lambda: lcap.proj_linear(x, w, out=y))
+    dq_med, mm_med = float(np.median(dq)), float(np.median(mm))
+    flops = 2.0 * t * n * k
+    dq_bytes = n * k * 3 + n * 4
+    del q, scale, x, w, y
+    return {"workload": f"projection y = x w^T, x bf16 [{t}, {k}], int8 weights [{n}, {k}] "
+                        "with per-row scales dequantized once to bf16",
+            "gemm_ms_median": round(mm_med, 5), "gemm_ms_min": round(float(mm.min()), 5),
+            "gemm_tflops": round(flops / (mm_med * 1e-3) / 1e12, 1),
+            "gemm_pct_bf16_peak": round(100 * flops / (mm_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "samples": int(mm.size), "calls_per_sample": reps,
+            "dequant_us_median": round(dq_med * 1e3, 2),
+            "dequant_hbm_gbs": round(dq_bytes / (dq_med * 1e-3) / 1e9, 1)}
+
+
 def gpu_clock():
     """Current shader clock as rocm-smi reports it (best effort, text)."""
     import subprocess
@@ -396,6 +427,10 @@ def main():
         others["gdn10k"] = gdn_step("gdn10k")
         others["gdn_packed"] = gdn_step("gdn_packed")
         torch.cuda.empty_cache()
+        # the 10k sequence's QKV (16 + 2 + 2 heads of 128) and output projections, hidden 2048
+        others["proj_qkv"] = proj_step(10240, 2560, 2048, seed=31)
+        others["proj_out"] = proj_step(10240, 2048, 2048, seed=32)
+        torch.cuda.empty_cache()
 
     sweep = None
     if args.sweep:
@@ -450,6 +485,8 @@ def main():
         line["decode_10k_cache_b64"] = others["decode_64"]
         line["gated_delta_rule_10k"] = others["gdn10k"]
         line["gated_delta_rule_packed"] = others["gdn_packed"]
+        line["projection_qkv_10k"] = others["proj_qkv"]
+        line["projection_out_10k"] = others["proj_out"]
         line["gpu_clock"] = gpu_clock()
     if sweep is not None:
         line["sweep_tflops_16x2_causal"] = sweep

@@ -16,6 +16,9 @@ functions carry the C entry points' names:
 * ``gdn_prefill(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None,
   out=None, final_state=False, workspace=None)`` -- chunked gated-delta-rule
   prefill (include/gdn_prefill.h), and ``gdn_prefill_workspace_size(...)``
+* ``proj_dequantize_int8(q, scale, out=None)`` and ``proj_linear(x, w,
+  out=None)`` -- int8 weights dequantized once to bf16, and y = x w^T by the
+  vendor GEMM (include/proj.h)
 
 There is no fallback: if the library is missing or cannot be loaded, the
 call raises.
@@ -28,7 +31,7 @@ import os
 
 __all__ = ["attn_prefill", "attn_prefill_check", "attn_prefill_kv", "attn_prefill_kv_check",
            "attn_decode", "attn_decode_workspace_size", "attn_strerror", "attn_version",
-           "gdn_prefill", "gdn_prefill_workspace_size",
+           "gdn_prefill", "gdn_prefill_workspace_size", "proj_dequantize_int8", "proj_linear",
            "AttnError", "library_path", "load_library", "ATTN_OK", "ATTN_EINVAL",
            "ATTN_EUNSUPPORTED", "ATTN_ELAUNCH", "ATTN_BF16", "ATTN_F32", "ATTN_CAUSAL",
            "ATTN_FULL", "ATTN_WINDOW"]
@@ -94,6 +97,11 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_prefill_workspace_size.argtypes = [ip, i32, i32, i32, i32, i32,
                                                ctypes.POINTER(ctypes.c_uint64)]
     lib.gdn_prefill_workspace_size.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.proj_dequantize_int8.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.proj_dequantize_int8.restype = ctypes.c_int
+    lib.proj_linear.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    lib.proj_linear.restype = ctypes.c_int
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -386,3 +394,53 @@ def gdn_prefill(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None, ou
     if status != ATTN_OK:
         raise AttnError(status, "gdn_prefill")
     return out if fin is None else (out, fin)
+
+
+def _handle(stream, device):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream or 0))
+
+
+def proj_dequantize_int8(q, scale, out=None, stream=None):
+    """bf16 weights w[n][k] = scale[n] * q[n][k] from int8 q [N, K] and float32 scale [N]."""
+    import torch
+
+    if q.dim() != 2 or q.dtype != torch.int8 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous int8 [N, K] tensor")
+    if scale.dtype != torch.float32 or tuple(scale.shape) != (q.shape[0],) or not scale.is_contiguous():
+        raise ValueError("scale must be a contiguous float32 [N] tensor")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor of q's shape")
+    status = load_library().proj_dequantize_int8(q.data_ptr(), scale.data_ptr(), out.data_ptr(),
+                                                 int(q.shape[0]), int(q.shape[1]),
+                                                 _handle(stream, q.device))
+    if status != ATTN_OK:
+        raise AttnError(status, "proj_dequantize_int8")
+    return out
+
+
+def proj_linear(x, w, out=None, stream=None):
+    """y = x w^T: x bf16 [T, K], w bf16 [N, K] -> y bf16 [T, N] (vendor GEMM, fp32 accumulation)."""
+    import torch
+
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("x must be [T, K] and w [N, K]")
+    for name, t in (("x", x), ("w", w)):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor")
+    T, K = (int(s) for s in x.shape)
+    N = int(w.shape[0])
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (T, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 [T, N] tensor")
+    status = load_library().proj_linear(x.data_ptr(), w.data_ptr(), out.data_ptr(), T, N, K,
+                                        _handle(stream, x.device))
+    if status != ATTN_OK:
+        raise AttnError(status, "proj_linear")
+    return out

@@ -1,9 +1,9 @@
 """Build the HIP library in-tree: ``python -m long_context_attention_prefill_amd.build``.
 
 Produces ``long_context_attention_prefill_amd/libattn_prefill.so`` for gfx950:
-the kernels (csrc/attn_fwd.hip, csrc/attn_decode.hip, csrc/gdn_fwd.hip)
-compiled by hipcc, the host-only C ABI (csrc/attn_api.cpp, csrc/gdn_api.cpp)
-compiled by g++, linked by hipcc.
+the kernels (csrc/*.hip) compiled by hipcc, the host-only C ABI
+(csrc/*_api.cpp) compiled by g++, linked by hipcc against rocBLAS (the
+vendor GEMM of the projections).
 """
 from __future__ import annotations
 
@@ -20,9 +20,12 @@ LIBRARY = os.path.join(PKG, "libattn_prefill.so")
 ARCH = "gfx950"
 
 # Kernel sources: attention prefill (both families), decode, gated delta rule.
-DEVICE_SOURCES = ("attn_fwd.hip", "attn_decode.hip", "gdn_fwd.hip")
+DEVICE_SOURCES = ("attn_fwd.hip", "attn_decode.hip", "gdn_fwd.hip", "proj_fwd.hip")
 # Host-only sources (C ABI: checks and planning), compiled by g++.
-HOST_SOURCES = ("attn_api.cpp", "gdn_api.cpp")
+HOST_SOURCES = ("attn_api.cpp", "gdn_api.cpp", "proj_api.cpp")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+# the projections call the vendor GEMM
+LINK_LIBS = ["-L" + os.path.join(ROCM, "lib"), "-lrocblas"]
 
 # Packed-fp32 VALU forms are kept out of every kernel on purpose.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -48,7 +51,8 @@ def build(verbose: bool = False, output: str = LIBRARY, extra_device_flags=()) -
         objs = []
         for src in HOST_SOURCES:
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
-            _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", *inc, "-c",
+            _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", *inc,
+                  "-isystem", os.path.join(ROCM, "include"), "-D__HIP_PLATFORM_AMD__", "-c",
                   os.path.join(CSRC, src), "-o", obj], verbose)
             objs.append(obj)
         for src in DEVICE_SOURCES:
@@ -57,7 +61,8 @@ def build(verbose: bool = False, output: str = LIBRARY, extra_device_flags=()) -
                   *extra_device_flags, *inc, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
             objs.append(obj)
         tmp_out = output + ".tmp"
-        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_out, *objs], verbose)
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_out, *objs, *LINK_LIBS,
+              "-Wl,-rpath," + os.path.join(ROCM, "lib")], verbose)
         os.replace(tmp_out, output)
     return output
 

@@ -43,10 +43,11 @@ def max_err(a, b):
 
 
 # log-sum-exp tolerance: the bf16 path sums bf16-rounded probabilities (each
-# within 2^-9 relative), so ln(sum) is within 2^-9 of exact; 2^-8 leaves a
-# factor 2 for the fp32 score and exp2 rounding.  The fp32 path sums fp32
+# within 2^-8 relative: round to nearest keeps 8 significant bits), so
+# ln(sum) is within about 2^-8 of exact; 2^-7 leaves a factor 2 for the fp32
+# score and exp2 rounding.  The fp32 path sums fp32
 # probabilities: within n * 2^-24 relative, < 1e-4 for the sizes tested.
-LSE_TOL = {"bf16": 2.0 ** -8, "f32": 1e-4}
+LSE_TOL = {"bf16": 2.0 ** -7, "f32": 1e-4}
 
 
 def run_hip_kv(q, k, v, cu_q, cu_k, mask, scale, dtype, lse=True):

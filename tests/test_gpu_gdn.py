@@ -2,9 +2,10 @@
 through the C ABI, on the same seeded inputs.
 
 Tolerance.  The kernels round six operand kinds to bf16 before MFMA products
-(2^-9 relative each): the chunk's inverse system T, the WY combinations W and
-U, the gated scores P, the decayed keys, the state S entering each chunk and
-the corrected values U'; sums are fp32.  A numpy replay of exactly those
+(within 2^-8 relative each: round to nearest keeps 8 significant bits): the
+chunk's inverse system T, the WY combinations W and U, the gated scores P,
+the decayed keys, the state S entering each chunk and the corrected values
+U'; sums are fp32.  A numpy replay of exactly those
 roundings on these input distributions (unit-norm q and k, v ~ N(0, 1),
 alpha ~ U(0.85, 1), beta ~ U(0, 1), up to 10240 tokens) stays within 0.8 % of
 max |o| (max abs error) and 0.4 % of rms(o) (rms error).  The bars below are
