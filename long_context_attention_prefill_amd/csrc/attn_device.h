@@ -59,9 +59,14 @@ constexpr uint32_t kOutOfRange = 0x7ffffff0u;
 
 template <int D>
 struct FastLayout {
-  static constexpr int CH = D / 8;        // 16-byte chunks of a row in memory
-  static constexpr int SLOTS = CH + 1;    // 16-byte slots per K or V row in LDS
+  static constexpr int CH = D / 8;            // 16-byte chunks of a row in memory
+  static constexpr int KST = (D + 15) / 16;   // 16-wide MFMA k steps over the row
+  // 16-byte slots per K or V row in LDS: the k steps' 2 KST chunks (those
+  // past CH zero-filled, so a head dim that is not a multiple of 16 reads
+  // zeros in its last step) plus one, an odd count
+  static constexpr int SLOTS = 2 * KST + 1;
   static constexpr int ROWB = SLOTS * 16;
+  static_assert(D % 8 == 0, "whole 16-byte chunks per row");
 };
 
 // Key (0..31 within a 32-key block) held by MFMA row m of S^T.

@@ -12,8 +12,9 @@
 // Scores are computed transposed, S^T = K Q^T, so each lane owns one query
 // column and 16 keys of each 32x32 block: the row max and row sum are mostly
 // in-lane, and the probabilities already sit in the B-operand layout of
-// O^T = V^T P^T.  V is transposed on its way into LDS (4 keys packed per
-// 8-byte store, XOR-swizzled rows) so PV operands are plain 16-byte reads.
+// O^T = V^T P^T, whose V^T operand comes from LDS through transposing reads.
+// head_dim 72 runs five 16-wide k steps (the last half over zero padding in
+// LDS) and three 32-row blocks of O^T (rows past 72 are dropped).
 //
 // fp32 family: vector-ALU kernel, two lanes per query row, K/V tiles in LDS.
 //
@@ -102,322 +103,7 @@ __device__ __forceinline__ void row_range(int mask, int W, int i, int n, int &lo
 
 
 // ---------------------------------------------------------------------------
-// bf16 / MFMA family
-// ---------------------------------------------------------------------------
-
-// Position of key group kg (4 keys) inside a 16-key chunk of a V^T row.  The
-// S^T accumulator gives lane half g the keys {4g..4g+3, 8+4g..8+4g+3} of
-// each 16; storing key groups in the order 0, 2, 1, 3 makes those 8 keys
-// contiguous, so one 16-byte read yields the A operand of O^T = V^T P^T.
-__device__ __forceinline__ int vt_pos(int kg) {
-  return ((kg >> 2) << 4) | ((kg & 1) << 3) | ((kg & 2) << 1);
-}
-
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_generic(const LaunchArgs a) {
-  constexpr int NT = NW * 64;
-  constexpr int BM = NW * 32;            // query rows per workgroup
-  constexpr int BN = 64;                 // keys per tile
-  constexpr int DK = (D + 15) / 16 * 16; // head dim padded to the MFMA K step
-  constexpr int KSTEPS = DK / 16;
-  constexpr int DV = (D + 31) / 32 * 32; // head dim padded to 32-row output blocks
-  constexpr int DBLK = DV / 32;
-  constexpr int CH = D / 8;              // 16-byte chunks per row in memory
-  constexpr int KROW = DK + 8;           // bf16 per K row in LDS (16 B pad)
-  constexpr int VROW_DW = (BN + 8) / 2;  // dwords per V^T row in LDS (16 B pad)
-  constexpr int KBUF = BN * KROW;        // bf16 per K buffer
-  constexpr int VBUF_DW = DV * VROW_DW;  // dwords per V^T buffer
-  constexpr int KUNITS = BN * CH;
-  constexpr int VUNITS = (BN / 4) * CH;
-  constexpr int KLOADS = (KUNITS + NT - 1) / NT;
-  constexpr int VLOADS = (VUNITS + NT - 1) / NT;
-  static_assert(BN == 64, "V^T swizzle assumes 8 chunks of 8 keys per row");
-
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2 * KBUF];
-  __shared__ __attribute__((aligned(16))) uint32_t vt_lds[2 * VBUF_DW];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
-
-  const Item it = decode_item(a, blockIdx.x);
-  const int s0q = a.q_start[it.seq], s0k = a.k_start[it.seq];
-  // queries are the last nq of nk positions: local row i sits at i + off
-  const int nq = a.q_len[it.seq], nk = a.k_len[it.seq], off = nk - nq;
-  const int h = it.head;
-  const int hk = h / a.group;
-  const int mask = a.mask_kind;
-  const int W = a.window;
-  const float c = a.c;
-  const bool neg = c < 0.0f;
-  const float cabs = neg ? -c : c;
-
-  const int q0 = it.tile * BM;
-  const int qend = min(q0 + BM, nq);
-  int kv_lo, kv_hi, tmp;
-  row_range(mask, W, q0 + off, nk, kv_lo, tmp);
-  row_range(mask, W, qend - 1 + off, nk, tmp, kv_hi);
-
-  const int wq0 = q0 + wave * 32;
-  const bool wave_active = wq0 < nq;
-  int w_lo = 0, w_hi = 0, i_lo = 0, i_hi = 0;
-  if (wave_active) {
-    const int wq1 = min(wq0 + 32, nq);
-    row_range(mask, W, wq0 + off, nk, w_lo, i_hi);
-    row_range(mask, W, wq1 - 1 + off, nk, i_lo, w_hi);
-  }
-  const int row = wq0 + l32;
-  const bool row_ok = row < nq;
-  int lo_r = 0, hi_r = 0;
-  if (row_ok) row_range(mask, W, row + off, nk, lo_r, hi_r);
-
-  // head-dim padding is read by the MFMAs and must hold zeros
-  if constexpr (DK != D) {
-    for (int u = tid; u < 2 * BN; u += NT) {
-      __bf16 *p = k_lds + u * KROW + D;
-#pragma unroll
-      for (int e = 0; e < DK - D; ++e) p[e] = (__bf16)0.0f;
-    }
-  }
-  if constexpr (DV != D) {
-    for (int u = tid; u < 2 * (DV - D) * VROW_DW; u += NT) {
-      const int b = u / ((DV - D) * VROW_DW);
-      const int r = u - b * (DV - D) * VROW_DW;
-      vt_lds[b * VBUF_DW + D * VROW_DW + r] = 0u;
-    }
-  }
-
-  // Q fragments: the B operand of S^T = K Q^T, lane (l32, g) holds
-  // q[row][16*kk + 8*g .. +7].
-  bf16x8 qf[KSTEPS];
-  {
-    const __bf16 *qrow = reinterpret_cast<const __bf16 *>(a.q) +
-                         ((size_t)(s0q + (row_ok ? row : 0)) * a.hq + h) * D;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const int d0 = 16 * kk + 8 * g;
-      if (row_ok && d0 < D)
-        qf[kk] = *reinterpret_cast<const bf16x8 *>(qrow + d0);
-      else
-        qf[kk] = (bf16x8)((__bf16)0.0f);
-    }
-  }
-
-  const size_t kv_rs = (size_t)a.hkv * D;  // elements between consecutive tokens
-  const __bf16 *kbase = reinterpret_cast<const __bf16 *>(a.k) + (size_t)s0k * kv_rs + (size_t)hk * D;
-  const __bf16 *vbase = reinterpret_cast<const __bf16 *>(a.v) + (size_t)s0k * kv_rs + (size_t)hk * D;
-
-  u32x4 kreg[KLOADS];
-  u32x4 vreg[VLOADS][4];
-
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int r = 0; r < KLOADS; ++r) {
-      const int u = tid + r * NT;
-      kreg[r] = (u32x4)(0u);
-      if (u < KUNITS) {
-        const int key = u / CH, ch = u - (u / CH) * CH;
-        const int j = kt + key;
-        if (j < kv_hi) kreg[r] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)j * kv_rs + ch * 8);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < VLOADS; ++r) {
-      const int u = tid + r * NT;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) vreg[r][rr] = (u32x4)(0u);
-      if (u < VUNITS) {
-        const int kg = u / CH, dg = u - (u / CH) * CH;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int j = kt + 4 * kg + rr;
-          if (j < kv_hi)
-            vreg[r][rr] = *reinterpret_cast<const u32x4 *>(vbase + (size_t)j * kv_rs + dg * 8);
-        }
-      }
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-    __bf16 *kb = k_lds + buf * KBUF;
-#pragma unroll
-    for (int r = 0; r < KLOADS; ++r) {
-      const int u = tid + r * NT;
-      if (u < KUNITS) {
-        const int key = u / CH, ch = u - (u / CH) * CH;
-        *reinterpret_cast<u32x4 *>(kb + key * KROW + ch * 8) = kreg[r];
-      }
-    }
-    uint32_t *vb = vt_lds + buf * VBUF_DW;
-#pragma unroll
-    for (int r = 0; r < VLOADS; ++r) {
-      const int u = tid + r * NT;
-      if (u < VUNITS) {
-        const int kg = u / CH, dg = u - (u / CH) * CH;
-        const int pos = vt_pos(kg);
-        const int chunk = pos >> 3, half = (pos >> 2) & 1;
-        const int col = 4 * (chunk ^ (dg & 7)) + 2 * half;  // row d = 8*dg + e: (d >> 3) & 7 == dg & 7
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t a0 = vreg[r][0][p], a1 = vreg[r][1][p];
-          const uint32_t a2 = vreg[r][2][p], a3 = vreg[r][3][p];
-          u32x2 lo, hi;  // d = 8*dg + 2p (low halves) and 8*dg + 2p + 1 (high halves)
-          lo[0] = (a0 & 0xffffu) | (a1 << 16);
-          lo[1] = (a2 & 0xffffu) | (a3 << 16);
-          hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-          hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-          const int d = 8 * dg + 2 * p;
-          *reinterpret_cast<u32x2 *>(vb + d * VROW_DW + col) = lo;
-          *reinterpret_cast<u32x2 *>(vb + (d + 1) * VROW_DW + col) = hi;
-        }
-      }
-    }
-  };
-
-  f32x16 o[DBLK];
-#pragma unroll
-  for (int db = 0; db < DBLK; ++db) o[db] = (f32x16)(0.0f);
-  float m_run = row_ok ? kNegInf : 0.0f;  // reference maximum, exp2 units
-  float l_run = 0.0f;                     // this lane's share of the row sum
-
-  auto compute = [&](int kt, int buf) {
-    const bool need_mask = kt < i_lo || kt + BN > i_hi;
-    const __bf16 *kb = k_lds + buf * KBUF;
-    f32x16 s[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      s[nb] = (f32x16)(0.0f);
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8 *>(kb + (nb * 32 + l32) * KROW + 16 * kk + 8 * g);
-        s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[nb], 0, 0, 0);
-      }
-    }
-    // row maximum of this tile (sign folded in: max of c*s), exp2 units
-    float mx = kNegInf;
-    bool any = true;
-    if (!need_mask) {
-      if (neg) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, -s[nb][j]);
-      } else {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[nb][j]);
-      }
-    } else {
-      any = row_ok && kt < hi_r && kt + BN > lo_r;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = kt + nb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-          const bool vis = key >= lo_r && key < hi_r;
-          const float sv = neg ? -s[nb][j] : s[nb][j];
-          mx = vis ? fmaxf(mx, sv) : mx;
-        }
-    }
-    float mt = any ? mx * cabs : kNegInf;
-    mt = fmaxf(mt, xor32(mt));
-    const bool raise = mt > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(raise)) {
-      const float m_new = raise ? mt : m_run;
-      const float alpha = raise ? fast_exp2(m_run - m_new) : 1.0f;
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = -m_run;
-    float lsum = 0.0f;
-    if (!need_mask) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float p = fast_exp2(__builtin_fmaf(s[nb][j], c, neg_m));
-          s[nb][j] = p;
-          lsum += p;
-        }
-    } else {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = kt + nb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-          const bool vis = key >= lo_r && key < hi_r;
-          const float p = vis ? fast_exp2(__builtin_fmaf(s[nb][j], c, neg_m)) : 0.0f;
-          s[nb][j] = p;
-          lsum += p;
-        }
-    }
-    l_run += lsum;
-    // P^T fragments (B operand of O^T = V^T P^T): k step ks covers keys
-    // 16ks .. 16ks+15 of the tile, i.e. accumulator entries 8*(ks&1)..+7 of
-    // block ks>>1.
-    bf16x8 pf[BN / 16];
-#pragma unroll
-    for (int ks = 0; ks < BN / 16; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[ks][e] = (__bf16)s[ks >> 1][8 * (ks & 1) + e];
-    const uint32_t *vb = vt_lds + buf * VBUF_DW;
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      const int d = 32 * db + l32;
-      const int sw = (d >> 3) & 7;
-#pragma unroll
-      for (int ks = 0; ks < BN / 16; ++ks) {
-        const bf16x8 vf =
-            *reinterpret_cast<const bf16x8 *>(vb + d * VROW_DW + 4 * ((2 * ks + g) ^ sw));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
-      }
-    }
-  };
-
-  const int ntiles = (kv_hi - kv_lo + BN - 1) / BN;
-  load_tile(kv_lo);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int kt = kv_lo + t * BN;
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile(kt + BN);
-    if (wave_active && kt < w_hi && kt + BN > w_lo) compute(kt, t & 1);
-    if (more) store_tile((t + 1) & 1);
-    __syncthreads();
-  }
-
-  if (wave_active) {
-    const float l_tot = l_run + xor32(l_run);
-    if (row_ok) {
-      const float inv = 1.0f / l_tot;
-      if (a.lse != nullptr && g == 0)
-        a.lse[(size_t)(s0q + row) * a.hq + h] = (m_run + log2f(l_tot)) * kLn2;
-      __bf16 *orow = reinterpret_cast<__bf16 *>(a.out) + ((size_t)(s0q + row) * a.hq + h) * D;
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int d = 32 * db + 8 * jj + 4 * g;
-          if (d < D) {
-            bf16x4 w;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * jj + e] * inv);
-            *reinterpret_cast<bf16x4 *>(orow + d) = w;
-          }
-        }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// bf16 / MFMA family, head_dim 64 and 128.  K and V reach LDS by direct
+// bf16 / MFMA family, head_dim 64, 72 and 128.  K and V reach LDS by direct
 // buffer->LDS loads: no staging registers, and rows past the key range read
 // as zeros (buffer range check).  Both tiles use the padded, key-permuted
 // layout of attn_device.h, whose K row reads and V transposing reads are
@@ -437,14 +123,14 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
   // The host pass only needs this kernel's signature for its launch stub;
   // the body (gfx950-only builtins) is compiled for the device alone.
 #if defined(__HIP_DEVICE_COMPILE__)
-  static_assert(D == 64 || D == 128, "fast path covers head_dim 64 and 128");
+  static_assert(D == 64 || D == 72 || D == 128, "fast path covers head_dim 64, 72 and 128");
   static_assert(R == 1 || R == 2, "one or two query sub-blocks per wave");
   using L = FastLayout<D>;
   constexpr int BM = NW * 32 * R;
   constexpr int BN = 64;
   constexpr int CH = L::CH;
-  constexpr int KST = D / 16;  // MFMA k steps of S^T
-  constexpr int DB = D / 32;   // 32-row blocks of O^T
+  constexpr int KST = L::KST;         // MFMA k steps of S^T (the last one zero-padded when D = 72)
+  constexpr int DB = (D + 31) / 32;  // 32-row blocks of O^T (rows past D are computed and dropped)
   constexpr int KBUF = BN * L::ROWB;  // bytes per K (or V) tile
   // A tile is NLOADS wave-wide direct loads (64 lanes x 16 bytes); each wave
   // issues NL of them, and a wave whose last load falls past the tile sends
@@ -527,8 +213,8 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
                          ((size_t)(s0q + (row_ok[r] ? row[r] : 0)) * a.hq + h) * D;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk)
-      qf[r][kk] = row_ok[r] ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * kk + 8 * g)
-                            : (bf16x8)((__bf16)0.0f);
+      qf[r][kk] = row_ok[r] && 16 * kk + 8 * g < D ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * kk + 8 * g)
+                                                   : (bf16x8)((__bf16)0.0f);
   }
 
   // Direct loads: wave-wide load j fills LDS slots 64j .. 64j+63 of a tile;
@@ -880,7 +566,9 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) bad = bad || (row_ok[r] && !__builtin_isfinite(o[r][db][j]));
+          for (int j = 0; j < 16; ++j)
+            bad = bad || (row_ok[r] && 32 * db + 8 * (j >> 2) + 4 * g + (j & 3) < D &&
+                          !__builtin_isfinite(o[r][db][j]));
       }
     }
     if (!__syncthreads_or(bad)) break;
@@ -902,6 +590,7 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int d = 32 * db + 8 * jj + 4 * g;
+            if (d >= D) continue;  // padding rows of O^T
             bf16x4 w;
 #pragma unroll
             for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[r][db][4 * jj + e] * inv);
@@ -1068,7 +757,7 @@ int rows_per_workgroup_f32(int) { return 128; }
 int launch_bf16(const LaunchArgs &a, int head_dim, void *stream) {
   switch (head_dim) {
     case 64: return launch(fwd_bf16_fast<64, kWavesBf16, 1>, a, kWavesBf16 * 64, stream);
-    case 72: return launch(fwd_bf16_generic<72, kWavesBf16>, a, kWavesBf16 * 64, stream);
+    case 72: return launch(fwd_bf16_fast<72, kWavesBf16, 1>, a, kWavesBf16 * 64, stream);
     case 128: return launch(fwd_bf16_fast<128, kWavesBf16, 1>, a, kWavesBf16 * 64, stream);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
