@@ -29,7 +29,8 @@
  * All four share one element type (ATTN_BF16 or ATTN_F32).  Device pointers
  * must be 16-byte aligned.  bf16 inputs are multiplied on matrix cores with
  * fp32 accumulation and a fp32 softmax; the output is rounded to bf16 (nearest
- * even).  fp32 inputs are computed in fp32 on the vector ALUs.
+ * even).  fp32 inputs are computed in fp32 on the fp32 matrix cores (exact
+ * products, fp32 sums).
  *
  * Ownership: the caller owns every buffer.  cu_seqlens is a HOST array read
  * only during the call.  The library allocates no device memory, holds no

@@ -16,7 +16,9 @@
 // head_dim 72 runs five 16-wide k steps (the last half over zero padding in
 // LDS) and three 32-row blocks of O^T (rows past 72 are dropped).
 //
-// fp32 family: vector-ALU kernel, two lanes per query row, K/V tiles in LDS.
+// fp32 family: v_mfma_f32_32x32x2_f32 (exact fp32 products, fp32 sums), the
+// scores kept in registers as the B operand of the PV product, V transposed
+// in LDS.
 //
 // A sequence holds nq queries and nk >= nq keys; its queries are the last nq
 // positions, so local query row r sits at position i = r + (nk - nq) (equal
@@ -603,140 +605,196 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
 }
 
 // ---------------------------------------------------------------------------
-// fp32 / vector-ALU family
+// fp32 / matrix-core family: v_mfma_f32_32x32x2_f32, exact fp32 products with
+// fp32 accumulation (157.3 TFLOP/s peak against 78.6 for unpacked vector
+// FMAs).  One workgroup per (sequence, query head, 128 query rows), four
+// waves of 32 rows; 32-key tiles.
+//   S^T = K Q^T: step s of the D/2 k steps takes column s from lane half 0
+//   and column s + D/2 from lane half 1, so each lane's q values and K row
+//   reads are contiguous (16-byte LDS reads feed four steps).
+//   O^T = V^T P^T: the scores stay in registers as the B operand -- step t
+//   of 16 takes, in lane half g, the key of accumulator element t
+//   (8 (t >> 2) + 4 g + (t & 3)) -- and V is stored transposed in LDS,
+//   [d][key], so four steps' V^T values are one 16-byte read.
+// Online softmax per tile in exp2 units with the lazy rescale; rows past D
+// (head dim 72 takes three 32-row blocks) are computed over zero rows of
+// V^T and dropped.
 // ---------------------------------------------------------------------------
 
 template <int D>
-__global__ __launch_bounds__(256) void fwd_f32(const LaunchArgs a) {
-  constexpr int NT = 256;
-  constexpr int BM = NT / 2;  // two lanes per query row
+__global__ __launch_bounds__(256, 2) void fwd_f32_mfma(const LaunchArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(D % 8 == 0, "head dim in whole float4 pairs");
   constexpr int BN = 32;
-  constexpr int DH = D / 2;   // elements per lane
-  constexpr int HROW = DH + 4;  // the two halves of a row sit in different banks
-  constexpr int ROW = 2 * HROW;
-  constexpr int F4 = D / 4;
-  static_assert(DH % 4 == 0, "half rows must be float4 aligned");
-
-  __shared__ __attribute__((aligned(16))) float k_lds[BN * ROW];
-  __shared__ __attribute__((aligned(16))) float v_lds[BN * ROW];
+  constexpr int H2 = D / 2;             // k steps of S^T
+  constexpr int DB = (D + 31) / 32;     // 32-row blocks of O^T
+  constexpr int KROW = D + 4;           // K tile row stride (floats); odd multiple of 16 bytes
+  constexpr int VROW = BN + 4;          // V^T tile row stride (floats)
+  constexpr int KT_F = BN * KROW, VT_F = DB * 32 * VROW;
+  constexpr int NF4 = BN * D / 4;           // float4s of a K (or V) tile
+  constexpr int LOADS = (NF4 + 255) / 256;  // per thread (the last round partial for D = 72)
+  __shared__ __attribute__((aligned(16))) float k_lds[2][KT_F];
+  __shared__ __attribute__((aligned(16))) float v_lds[2][VT_F];
 
   const int tid = threadIdx.x;
-  const int half = tid & 1;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
   const Item it = decode_item(a, blockIdx.x);
   const int s0q = a.q_start[it.seq], s0k = a.k_start[it.seq];
-  // queries are the last nq of nk positions: local row i sits at i + off
   const int nq = a.q_len[it.seq], nk = a.k_len[it.seq], off = nk - nq;
   const int h = it.head;
   const int hk = h / a.group;
   const int mask = a.mask_kind;
   const int W = a.window;
-  const float c = a.c;
+  const float c = a.c == 0.0f ? 0x1p-126f : a.c;  // scale 0: every weight exp2(~0) = 1
 
-  const int q0 = it.tile * BM;
-  const int qend = min(q0 + BM, nq);
+  const int q0 = it.tile * 128;
+  const int qend = min(q0 + 128, nq);
   int kv_lo, kv_hi, tmp;
   row_range(mask, W, q0 + off, nk, kv_lo, tmp);
   row_range(mask, W, qend - 1 + off, nk, tmp, kv_hi);
 
-  const int row = q0 + (tid >> 1);
+  const int row = q0 + 32 * wave + l32;
   const bool row_ok = row < nq;
   int lo_r = 0, hi_r = 0;
   if (row_ok) row_range(mask, W, row + off, nk, lo_r, hi_r);
 
-  float qv[DH], o[DH];
+  // q[row][s + g D/2], s = 0 .. D/2 - 1
+  float qv[H2];
   {
     const float *qrow = reinterpret_cast<const float *>(a.q) +
-                        ((size_t)(s0q + (row_ok ? row : 0)) * a.hq + h) * D + half * DH;
+                        ((size_t)(s0q + (row_ok ? row : 0)) * a.hq + h) * D + g * H2;
 #pragma unroll
-    for (int e = 0; e < DH; e += 4) {
-      f32x4 x = row_ok ? *reinterpret_cast<const f32x4 *>(qrow + e) : (f32x4)(0.0f);
-      qv[e] = x[0];
-      qv[e + 1] = x[1];
-      qv[e + 2] = x[2];
-      qv[e + 3] = x[3];
+    for (int s4 = 0; s4 < H2; s4 += 4) {
+      const f32x4 x = row_ok ? *reinterpret_cast<const f32x4 *>(qrow + s4) : (f32x4)(0.0f);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[s4 + e] = x[e];
     }
-#pragma unroll
-    for (int e = 0; e < DH; ++e) o[e] = 0.0f;
   }
-  float m_run = kNegInf, l_run = 0.0f;
+
+  // V^T rows past D stay zero in both buffers
+  for (int i = tid; i < (DB * 32 - D) * VROW; i += 256) {
+    v_lds[0][D * VROW + i] = 0.0f;
+    v_lds[1][D * VROW + i] = 0.0f;
+  }
 
   const size_t kv_rs = (size_t)a.hkv * D;
   const float *kbase = reinterpret_cast<const float *>(a.k) + (size_t)s0k * kv_rs + (size_t)hk * D;
   const float *vbase = reinterpret_cast<const float *>(a.v) + (size_t)s0k * kv_rs + (size_t)hk * D;
-
-  for (int kt = kv_lo; kt < kv_hi; kt += BN) {
-    __syncthreads();  // previous tile fully consumed
-    for (int u = tid; u < BN * F4; u += NT) {
-      const int key = u / F4, col = (u - key * F4) * 4;
-      const int j = kt + key;
-      f32x4 kx = (f32x4)(0.0f), vx = (f32x4)(0.0f);
-      if (j < kv_hi) {
-        kx = *reinterpret_cast<const f32x4 *>(kbase + (size_t)j * kv_rs + col);
-        vx = *reinterpret_cast<const f32x4 *>(vbase + (size_t)j * kv_rs + col);
-      }
-      const int hh = col / DH, cc = col - hh * DH;
-      *reinterpret_cast<f32x4 *>(k_lds + key * ROW + hh * HROW + cc) = kx;
-      *reinterpret_cast<f32x4 *>(v_lds + key * ROW + hh * HROW + cc) = vx;
+  // tile kt: thread loads float4 u = tid + 256 i of K and of V (key u / (D/4))
+  f32x4 kr[LOADS], vr[LOADS];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int u = min(tid + 256 * i, NF4 - 1);  // a partial last round repeats the final float4
+      const int key = u / (D / 4), col = (u % (D / 4)) * 4;
+      const int j = min(kt + key, kv_hi - 1);  // rows past the range are masked in the scores
+      kr[i] = *reinterpret_cast<const f32x4 *>(kbase + (size_t)j * kv_rs + col);
+      vr[i] = *reinterpret_cast<const f32x4 *>(vbase + (size_t)j * kv_rs + col);
+      if (kt + key >= kv_hi) vr[i] = (f32x4)(0.0f);  // their probabilities are 0; keep V finite
     }
-    __syncthreads();
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int u = min(tid + 256 * i, NF4 - 1);  // repeats write the same values again
+      const int key = u / (D / 4), col = (u % (D / 4)) * 4;
+      *reinterpret_cast<f32x4 *>(&k_lds[buf][key * KROW + col]) = kr[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v_lds[buf][(col + e) * VROW + key] = vr[i][e];
+    }
+  };
 
-    float x[BN];
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16)(0.0f);
+  float m_run = kNegInf, l_run = 0.0f;  // reference (exp2 units), this lane's share of the sum
+
+  int buf = 0;
+  if (kv_lo < kv_hi) {
+    load_tile(kv_lo);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int kt = kv_lo; kt < kv_hi; kt += BN) {
+    const bool more = kt + BN < kv_hi;
+    if (more) load_tile(kt + BN);
+    // S^T block: keys kt .. kt+31 (rows) x this wave's 32 queries (columns)
+    f32x16 sc = (f32x16)(0.0f);
+    {
+      const float *krow = &k_lds[buf][l32 * KROW + g * H2];
+#pragma unroll
+      for (int s4 = 0; s4 < H2; s4 += 4) {
+        const f32x4 kx = *reinterpret_cast<const f32x4 *>(krow + s4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sc = __builtin_amdgcn_mfma_f32_32x32x2f32(kx[e], qv[s4 + e], sc, 0, 0, 0);
+      }
+    }
+    // mask, reference, probabilities (element e: key kt + 8 (e >> 2) + 4 g + (e & 3))
     float mt = kNegInf;
 #pragma unroll
-    for (int jj = 0; jj < BN; ++jj) {
-      const float *kr = k_lds + jj * ROW + half * HROW;
-      float acc = 0.0f;
-#pragma unroll
-      for (int e = 0; e < DH; e += 4) {
-        const f32x4 kx = *reinterpret_cast<const f32x4 *>(kr + e);
-        acc = __builtin_fmaf(qv[e], kx[0], acc);
-        acc = __builtin_fmaf(qv[e + 1], kx[1], acc);
-        acc = __builtin_fmaf(qv[e + 2], kx[2], acc);
-        acc = __builtin_fmaf(qv[e + 3], kx[3], acc);
-      }
-      acc += __shfl_xor(acc, 1);
-      const int key = kt + jj;
+    for (int e = 0; e < 16; ++e) {
+      const int key = kt + 8 * (e >> 2) + 4 * g + (e & 3);
       const bool vis = row_ok && key >= lo_r && key < hi_r;
-      x[jj] = vis ? acc * c : kNegInf;
-      mt = fmaxf(mt, x[jj]);
+      sc[e] = vis ? sc[e] * c : kNegInf;
+      mt = fmaxf(mt, sc[e]);
     }
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2(m_run - m_new);
+    mt = fmaxf(mt, xor32(mt));
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack)) {
+      const float m_new = mt > m_run + kRescaleSlack ? mt : m_run;
+      const float alpha = m_run == kNegInf ? 0.0f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int e = 0; e < DH; ++e) o[e] *= alpha;
-    l_run *= alpha;
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
 #pragma unroll
-    for (int jj = 0; jj < BN; ++jj) {
-      const float p = (x[jj] == kNegInf) ? 0.0f : fast_exp2(x[jj] - m_new);
-      l_run += p;
-      const float *vr = v_lds + jj * ROW + half * HROW;
+    for (int e = 0; e < 16; ++e) {
+      sc[e] = sc[e] == kNegInf ? 0.0f : fast_exp2(sc[e] - m_run);
+      l_run += sc[e];
+    }
+    // O^T += V^T P^T
 #pragma unroll
-      for (int e = 0; e < DH; e += 4) {
-        const f32x4 vx = *reinterpret_cast<const f32x4 *>(vr + e);
-        o[e] = __builtin_fmaf(p, vx[0], o[e]);
-        o[e + 1] = __builtin_fmaf(p, vx[1], o[e + 1]);
-        o[e + 2] = __builtin_fmaf(p, vx[2], o[e + 2]);
-        o[e + 3] = __builtin_fmaf(p, vx[3], o[e + 3]);
+    for (int db = 0; db < DB; ++db) {
+      const float *vrow = &v_lds[buf][(32 * db + l32) * VROW + 4 * g];
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const f32x4 vx = *reinterpret_cast<const f32x4 *>(vrow + 8 * t4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vx[e], sc[4 * t4 + e], o[db], 0, 0, 0);
       }
     }
-    m_run = m_new;
+    // the other buffer's last readers finished before the previous barrier
+    if (more) {
+      store_tile(buf ^ 1);
+      __syncthreads();
+    }
+    buf ^= 1;
   }
 
+  const float l_tot = l_run + xor32(l_run);
   if (row_ok) {
-    const float inv = 1.0f / l_run;
-    if (a.lse != nullptr && half == 0)
-      a.lse[(size_t)(s0q + row) * a.hq + h] = (m_run + log2f(l_run)) * kLn2;
-    float *orow = reinterpret_cast<float *>(a.out) + ((size_t)(s0q + row) * a.hq + h) * D + half * DH;
+    const float inv = 1.0f / l_tot;
+    if (a.lse != nullptr && g == 0) a.lse[(size_t)(s0q + row) * a.hq + h] = (m_run + log2f(l_tot)) * kLn2;
+    float *orow = reinterpret_cast<float *>(a.out) + ((size_t)(s0q + row) * a.hq + h) * D;
 #pragma unroll
-    for (int e = 0; e < DH; e += 4) {
-      f32x4 w;
-      w[0] = o[e] * inv;
-      w[1] = o[e + 1] * inv;
-      w[2] = o[e + 2] * inv;
-      w[3] = o[e + 3] * inv;
-      *reinterpret_cast<f32x4 *>(orow + e) = w;
-    }
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d = 32 * db + 8 * jj + 4 * g;
+        if (d >= D) continue;
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = o[db][4 * jj + e] * inv;
+        *reinterpret_cast<f32x4 *>(orow + d) = w;
+      }
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 template <typename K>
@@ -765,9 +823,9 @@ int launch_bf16(const LaunchArgs &a, int head_dim, void *stream) {
 
 int launch_f32(const LaunchArgs &a, int head_dim, void *stream) {
   switch (head_dim) {
-    case 64: return launch(fwd_f32<64>, a, 256, stream);
-    case 72: return launch(fwd_f32<72>, a, 256, stream);
-    case 128: return launch(fwd_f32<128>, a, 256, stream);
+    case 64: return launch(fwd_f32_mfma<64>, a, 256, stream);
+    case 72: return launch(fwd_f32_mfma<72>, a, 256, stream);
+    case 128: return launch(fwd_f32_mfma<128>, a, 256, stream);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
 }
