@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_TFLOPS = 157.3  # MI355X dense fp32 (matrix cores and vector ALUs alike)
 # sources the prefill kernels are compiled from (the traffic summary names their digest)
 KERNEL_SRCS = [os.path.join(ROOT, "long_context_attention_prefill_amd", "csrc", f)
                for f in ("attn_fwd.hip", "attn_device.h", "attn_launch.h")]
@@ -287,6 +288,44 @@ def proj_step(t, n, k, seed):
             "dequant_hbm_gbs": round(dq_bytes / (dq_med * 1e-3) / 1e9, 1)}
 
 
+def vision_step(name):
+    """vision_attention_block on a seeded multi-slice image: time per call and
+    the rate of its algorithmic flops (the two projections, 2 T hidden 4 H d,
+    plus full attention over each image, 4 n^2 H d) against the matrix-core
+    peak of its dtype."""
+    import torch
+
+    import long_context_attention_prefill_amd as lcap
+    from long_context_attention_prefill_amd import workloads as W
+
+    spec = W.VISION_WORKLOADS[name]
+    lens, hidden, H, d, dt = spec["lens"], spec["hidden"], spec["n_heads"], spec["d"], spec["dtype"]
+    tdt = torch.bfloat16 if dt == W.BF16 else torch.float32
+    dev = [torch.from_numpy(a).to(tdt).to("cuda")
+           for a in W.make_vision_inputs(lens, hidden, H, d, dt, spec["seed"])]
+    T = int(np.sum(lens))
+    cu = [0] + [int(x) for x in np.cumsum(lens)]
+    code = lcap.ATTN_BF16 if dt == W.BF16 else lcap.ATTN_F32
+    ws = torch.empty(lcap.vision_attention_block_workspace_size(T, H, d, hidden, code), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((T, hidden), dtype=tdt, device="cuda")
+    per_call, reps = event_samples(lambda: lcap.vision_attention_block(
+        *dev, cu, H, mask="full", out=out, workspace=ws))
+    med = float(np.median(per_call))
+    proj_flops = 2.0 * T * hidden * 4 * H * d
+    attn_flops = 4.0 * sum(n * n for n in lens) * H * d
+    peak = PEAK_BF16_TFLOPS if dt == W.BF16 else PEAK_F32_TFLOPS
+    tflops = (proj_flops + attn_flops) / (med * 1e-3) / 1e12
+    del dev, ws, out
+    return {"workload": f"vision attention block (QKV projection, full attention, output projection), "
+                        f"{len(lens)} images x {lens[0]} patches, hidden {hidden}, {H} heads of {d}, {dt}",
+            "ms_median": round(med, 5), "ms_min": round(float(per_call.min()), 5),
+            "samples": int(per_call.size), "calls_per_sample": reps,
+            "patches_per_s": round(T / (med * 1e-3), 1),
+            "algorithmic_flops": proj_flops + attn_flops, "tflops": round(tflops, 1),
+            "pct_peak": round(100 * tflops / peak, 2)}
+
+
 def gpu_clock():
     """Current shader clock as rocm-smi reports it (best effort, text)."""
     import subprocess
@@ -414,7 +453,7 @@ def main():
         stats10 = summarize(w10, *sample_calls(w10, dev10, host10[3]))
         others["chunked"] = chunked_prefill(w10, dev10, 2048)
         del dev10[:]
-        for key in ("2", "5a", "5b"):
+        for key in ("2", "4", "5a", "5b"):
             w = W.WORKLOADS[key]
             hst, dv = device_inputs(w)
             others[key] = summarize(w, *sample_calls(w, dv, hst[3]))
@@ -430,6 +469,9 @@ def main():
         # the 10k sequence's QKV (16 + 2 + 2 heads of 128) and output projections, hidden 2048
         others["proj_qkv"] = proj_step(10240, 2560, 2048, seed=31)
         others["proj_out"] = proj_step(10240, 2048, 2048, seed=32)
+        torch.cuda.empty_cache()
+        others["vision_bf16"] = vision_step("vision_slices_bf16")
+        others["vision_f32"] = vision_step("vision_slices_f32")
         torch.cuda.empty_cache()
 
     sweep = None
@@ -478,6 +520,7 @@ def main():
     if stats10 is not None:
         line["samples_10k"] = stats10
         line["at_2k"] = others["2"]
+        line["full_d72_1k"] = others["4"]
         line["packed_causal_5a"] = others["5a"]
         line["packed_window256_5b"] = others["5b"]
         line["chunked_prefill_10k"] = others["chunked"]
@@ -487,6 +530,8 @@ def main():
         line["gated_delta_rule_packed"] = others["gdn_packed"]
         line["projection_qkv_10k"] = others["proj_qkv"]
         line["projection_out_10k"] = others["proj_out"]
+        line["vision_block_bf16"] = others["vision_bf16"]
+        line["vision_block_f32"] = others["vision_f32"]
         line["gpu_clock"] = gpu_clock()
     if sweep is not None:
         line["sweep_tflops_16x2_causal"] = sweep

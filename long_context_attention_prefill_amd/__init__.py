@@ -19,6 +19,10 @@ functions carry the C entry points' names:
 * ``proj_dequantize_int8(q, scale, out=None)`` and ``proj_linear(x, w,
   out=None)`` -- int8 weights dequantized once to bf16, and y = x w^T by the
   vendor GEMM (include/proj.h)
+* ``vision_attention_block(x, w_qkv, b_qkv, w_o, b_o, cu_seqlens, n_heads,
+  mask="full", scale=None, out=None, workspace=None)`` -- QKV projection,
+  attention and output projection in one call (include/vision_block.h), and
+  ``vision_attention_block_workspace_size(...)``
 
 There is no fallback: if the library is missing or cannot be loaded, the
 call raises.
@@ -32,6 +36,7 @@ import os
 __all__ = ["attn_prefill", "attn_prefill_check", "attn_prefill_kv", "attn_prefill_kv_check",
            "attn_decode", "attn_decode_workspace_size", "attn_strerror", "attn_version",
            "gdn_prefill", "gdn_prefill_workspace_size", "proj_dequantize_int8", "proj_linear",
+           "vision_attention_block", "vision_attention_block_workspace_size",
            "AttnError", "library_path", "load_library", "ATTN_OK", "ATTN_EINVAL",
            "ATTN_EUNSUPPORTED", "ATTN_ELAUNCH", "ATTN_BF16", "ATTN_F32", "ATTN_CAUSAL",
            "ATTN_FULL", "ATTN_WINDOW"]
@@ -102,6 +107,13 @@ def load_library() -> ctypes.CDLL:
     lib.proj_dequantize_int8.restype = ctypes.c_int
     lib.proj_linear.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.proj_linear.restype = ctypes.c_int
+    f32, u64 = ctypes.c_float, ctypes.c_uint64
+    lib.vision_attention_block.argtypes = [vp, vp, vp, vp, vp, vp, ip, i32, i32, i32, i32, i32, i32,
+                                           i32, f32, vp, u64, vp]
+    lib.vision_attention_block.restype = ctypes.c_int
+    lib.vision_attention_block_workspace_size.argtypes = [i64, i32, i32, i32, i32,
+                                                          ctypes.POINTER(u64)]
+    lib.vision_attention_block_workspace_size.restype = ctypes.c_int
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -443,4 +455,63 @@ def proj_linear(x, w, out=None, stream=None):
                                         _handle(stream, x.device))
     if status != ATTN_OK:
         raise AttnError(status, "proj_linear")
+    return out
+
+
+def vision_attention_block_workspace_size(tokens, n_heads, head_dim, hidden, dtype=ATTN_BF16) -> int:
+    """Workspace bytes vision_attention_block needs for ``tokens`` packed tokens."""
+    out = ctypes.c_uint64(0)
+    status = load_library().vision_attention_block_workspace_size(int(tokens), int(n_heads), int(head_dim),
+                                                                  int(hidden), int(dtype), ctypes.byref(out))
+    if status != ATTN_OK:
+        raise AttnError(status, "vision_attention_block_workspace_size")
+    return int(out.value)
+
+
+def vision_attention_block(x, w_qkv, b_qkv, w_o, b_o, cu_seqlens, n_heads, mask="full", scale=None,
+                           out=None, workspace=None, stream=None):
+    """out = attention(x W_qkv^T + b_qkv) W_o^T + b_o over packed images.
+
+    x [T, hidden]; w_qkv [3 H d, hidden] (q, k, v row blocks, heads contiguous);
+    b_qkv [3 H d]; w_o [hidden, H d]; b_o [hidden]; all contiguous, one dtype
+    (bf16 or fp32).  cu_seqlens: host sequence of n_images+1 ints; mask "full",
+    "causal" or ("window", W); scale defaults to 1/sqrt(d).  A workspace tensor
+    (uint8, at least vision_attention_block_workspace_size bytes) is allocated
+    when none is given.
+    """
+    import torch
+
+    if x.dim() != 2 or w_qkv.dim() != 2 or w_o.dim() != 2 or b_qkv.dim() != 1 or b_o.dim() != 1:
+        raise ValueError("x, w_qkv, w_o must be 2-d and the biases 1-d")
+    T, hidden = (int(s) for s in x.shape)
+    H = int(n_heads)
+    if H <= 0 or w_qkv.shape[0] % (3 * H) != 0:
+        raise ValueError("w_qkv must have 3 * n_heads * head_dim rows")
+    d = int(w_qkv.shape[0]) // (3 * H)
+    if tuple(w_qkv.shape) != (3 * H * d, hidden) or tuple(b_qkv.shape) != (3 * H * d,) \
+            or tuple(w_o.shape) != (hidden, H * d) or tuple(b_o.shape) != (hidden,):
+        raise ValueError("weight shapes disagree with x and n_heads")
+    if out is None:
+        out = torch.empty_like(x)
+    for name, t in (("x", x), ("w_qkv", w_qkv), ("b_qkv", b_qkv), ("w_o", w_o), ("b_o", b_o), ("out", out)):
+        if t.dtype != x.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous and of x's dtype")
+    if tuple(out.shape) != (T, hidden):
+        raise ValueError("out must be [T, hidden]")
+    kind, window = _mask_args(mask)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _dtype_code(x)
+    cu, n_seqs = _cu_array(cu_seqlens)
+    if n_seqs >= 0 and int(cu[n_seqs]) != T:
+        raise ValueError("cu_seqlens[-1] must equal the number of packed tokens")
+    if workspace is None:
+        need = vision_attention_block_workspace_size(T, H, d, hidden, code)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    status = load_library().vision_attention_block(
+        x.data_ptr(), w_qkv.data_ptr(), b_qkv.data_ptr(), w_o.data_ptr(), b_o.data_ptr(), out.data_ptr(),
+        cu, n_seqs, H, d, hidden, code, kind, window, float(scale), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _handle(stream, x.device))
+    if status != ATTN_OK:
+        raise AttnError(status, "vision_attention_block")
     return out

@@ -30,6 +30,28 @@ rocblas_handle thread_handle() {
 
 }  // namespace
 
+namespace proj {
+
+int gemm_nt(const void *x, const void *w, void *y, int64_t t, int64_t n, int64_t k, bool f32_in,
+            bool f32_out, void *stream) {
+  rocblas_handle h = thread_handle();
+  if (h == nullptr) return -1;
+  if (rocblas_set_stream(h, static_cast<hipStream_t>(stream)) != rocblas_status_success) return -1;
+  // Row-major y[T][N] = x[T][K] w[N][K]^T is, column-major, the N x T matrix
+  // W^T X with W the K x N view of w (ld K) and X the K x T view of x (ld K).
+  const rocblas_datatype in = f32_in ? rocblas_datatype_f32_r : rocblas_datatype_bf16_r;
+  const rocblas_datatype out = f32_out ? rocblas_datatype_f32_r : in;
+  const float alpha = 1.0f, beta = 0.0f;
+  const rocblas_status st = rocblas_gemm_ex(
+      h, rocblas_operation_transpose, rocblas_operation_none, static_cast<rocblas_int>(n),
+      static_cast<rocblas_int>(t), static_cast<rocblas_int>(k), &alpha, w, in, static_cast<rocblas_int>(k), x, in,
+      static_cast<rocblas_int>(k), &beta, y, out, static_cast<rocblas_int>(n), y, out,
+      static_cast<rocblas_int>(n), rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+  return st == rocblas_status_success ? 0 : -1;
+}
+
+}  // namespace proj
+
 extern "C" {
 
 int proj_dequantize_int8(const int8_t *q, const float *scale, void *w, int64_t n, int64_t k,
@@ -53,19 +75,7 @@ int proj_linear(const void *x, const void *w, void *y, int64_t t, int64_t n, int
   const uint64_t xb = static_cast<uint64_t>(t) * k * 2, wb = static_cast<uint64_t>(n) * k * 2,
                  yb = static_cast<uint64_t>(t) * n * 2;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, w, wb)) return ATTN_EINVAL;
-  rocblas_handle h = thread_handle();
-  if (h == nullptr) return ATTN_ELAUNCH;
-  if (rocblas_set_stream(h, static_cast<hipStream_t>(stream)) != rocblas_status_success) return ATTN_ELAUNCH;
-  // Row-major y[T][N] = x[T][K] w[N][K]^T is, column-major, the N x T matrix
-  // W^T X with W the K x N view of w (ld K) and X the K x T view of x (ld K).
-  const float alpha = 1.0f, beta = 0.0f;
-  const rocblas_status st = rocblas_gemm_ex(
-      h, rocblas_operation_transpose, rocblas_operation_none, static_cast<rocblas_int>(n),
-      static_cast<rocblas_int>(t), static_cast<rocblas_int>(k), &alpha, w, rocblas_datatype_bf16_r,
-      static_cast<rocblas_int>(k), x, rocblas_datatype_bf16_r, static_cast<rocblas_int>(k), &beta, y,
-      rocblas_datatype_bf16_r, static_cast<rocblas_int>(n), y, rocblas_datatype_bf16_r,
-      static_cast<rocblas_int>(n), rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-  return st == rocblas_status_success ? ATTN_OK : ATTN_ELAUNCH;
+  return proj::gemm_nt(x, w, y, t, n, k, false, false, stream) == 0 ? ATTN_OK : ATTN_ELAUNCH;
 }
 
 }  // extern "C"

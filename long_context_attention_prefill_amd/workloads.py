@@ -246,3 +246,40 @@ GDN_WORKLOADS = {
     # the packed 4-sequence batch of the attention workloads
     "gdn_packed": dict(lens=[2048, 5120, 8192, 10240], n_heads=16, dk=128, dv=128, seed=22),
 }
+
+
+# ---------------------------------------------------------------------------
+# Vision tower attention block (the paper's SigLIP2 encoder layers: abstract,
+# result (iii); gist.science summary, Metodologia: FP32 vision weights).  The
+# pages give neither layer sizes nor image token counts; the shapes here are
+# SigLIP2's so400m encoder (hidden 1152, 16 heads of 72) and images of 768
+# patches (a 448 x 336 slice at 14-pixel patches), packed NaViT-style.
+# ---------------------------------------------------------------------------
+
+def make_vision_inputs(lens, hidden, n_heads, d, dtype, seed, qk_gain=1.5, bias_sigma=0.05):
+    """(x, w_qkv, b_qkv, w_o, b_o) for a packed batch of images of ``lens`` patches.
+
+    x ~ N(0, 1) (normalised activations); w_qkv ~ N(0, 1/hidden) with its q
+    and k row blocks times ``qk_gain`` (sharper attention than chance);
+    w_o ~ N(0, 1/(n_heads d)); both biases ~ N(0, bias_sigma^2).  Every array
+    is rounded to ``dtype``.  Draw order from ``Generator(PCG64(seed))``: x,
+    w_qkv, b_qkv, w_o, b_o, each C-order over its full shape.
+    """
+    T = int(np.sum(lens))
+    hd = n_heads * d
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((T, hidden))
+    w_qkv = rng.standard_normal((3 * hd, hidden)) / math.sqrt(hidden)
+    w_qkv[:2 * hd] *= qk_gain
+    b_qkv = rng.standard_normal(3 * hd) * bias_sigma
+    w_o = rng.standard_normal((hidden, hd)) / math.sqrt(hd)
+    b_o = rng.standard_normal(hidden) * bias_sigma
+    return tuple(round_to(a, dtype) for a in (x, w_qkv, b_qkv, w_o, b_o))
+
+
+VISION_WORKLOADS = {
+    # a multi-slice image: five slices of 768 patches, packed
+    "vision_slices_bf16": dict(lens=[768] * 5, hidden=1152, n_heads=16, d=72, dtype=BF16, seed=31),
+    # the same in fp32, the precision the pages keep the vision weights in
+    "vision_slices_f32": dict(lens=[768] * 5, hidden=1152, n_heads=16, d=72, dtype=F32, seed=32),
+}
