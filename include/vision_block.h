@@ -17,10 +17,12 @@
  * Layout (row-major, contiguous, all of `dtype`): x [T][hidden],
  * w_qkv [3 H d][hidden], b_qkv [3 H d], w_o [hidden][H d], b_o [hidden],
  * out [T][hidden]; T = cu_seqlens[n_seqs], sequences (images) independent.
- * The projections are the vendor GEMM with fp32 accumulation and fp32
- * results; the bias is added in fp32 and each of q, k, v and out is rounded
- * once to `dtype`; the attention is attn_prefill (fp32 inputs on the fp32
- * matrix cores, bf16 on the bf16 ones).
+ * The projections are the vendor GEMM (hipBLASLt) with fp32 accumulation and
+ * the bias added to the fp32 sums in its epilogue, so each of q, k, v and
+ * out is rounded once to `dtype`; the attention (attn_prefill's kernels:
+ * fp32 inputs on the fp32 matrix cores, bf16 on the bf16 ones) reads q, k
+ * and v in place as the three column blocks of the [T][3 H d] projection
+ * output, and its output is rounded to `dtype` before the output projection.
  *
  * Ownership and errors as for attn_prefill; the caller passes a workspace of
  * vision_attention_block_workspace_size() bytes (16-byte aligned, overlapping
@@ -45,7 +47,8 @@ extern "C" {
  * Returns ATTN_OK; ATTN_EINVAL for NULL or misaligned pointers (pointers may
  * be NULL only when T = 0), bad cu_seqlens, bad sizes or mask, overlap, or a
  * missing/small workspace; ATTN_EUNSUPPORTED for other head dims or dtypes or
- * sizes of 2^31 or more; ATTN_ELAUNCH when a launch or the vendor GEMM fails.
+ * sizes of 2^31 or more; ATTN_ELAUNCH when a launch fails or the vendor GEMM
+ * has no algorithm for the shape or refuses the call.
  */
 int vision_attention_block(const void *x, const void *w_qkv, const void *b_qkv,
                            const void *w_o, const void *b_o, void *out,
@@ -55,10 +58,10 @@ int vision_attention_block(const void *x, const void *w_qkv, const void *b_qkv,
                            float scale, void *workspace, uint64_t workspace_bytes,
                            void *stream);
 
-/* Workspace bytes for T tokens (host-only): T (3 H d + hidden) fp32 values for
- * the projections' fp32 results plus 4 T H d values of dtype for q, k, v and
- * the attention output.  Returns ATTN_EINVAL / ATTN_EUNSUPPORTED for bad
- * sizes, else ATTN_OK. */
+/* Workspace bytes for T tokens (host-only): 4 T H d values of dtype, the
+ * QKV projection output and the attention output (each rounded up to 256
+ * bytes).  Returns ATTN_EINVAL / ATTN_EUNSUPPORTED for bad sizes, else
+ * ATTN_OK. */
 int vision_attention_block_workspace_size(int64_t tokens, int32_t n_heads,
                                           int32_t head_dim, int32_t hidden,
                                           int32_t dtype, uint64_t *bytes);

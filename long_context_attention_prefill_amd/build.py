@@ -20,13 +20,13 @@ LIBRARY = os.path.join(PKG, "libattn_prefill.so")
 ARCH = "gfx950"
 
 # Kernel sources: attention prefill (both families), decode, gated delta rule,
-# projections, the vision block's elementwise passes.
-DEVICE_SOURCES = ("attn_fwd.hip", "attn_decode.hip", "gdn_fwd.hip", "proj_fwd.hip", "vision_fwd.hip")
+# projections (int8 dequantization).
+DEVICE_SOURCES = ("attn_fwd.hip", "attn_decode.hip", "gdn_fwd.hip", "proj_fwd.hip")
 # Host-only sources (C ABI: checks and planning), compiled by g++.
 HOST_SOURCES = ("attn_api.cpp", "gdn_api.cpp", "proj_api.cpp", "vision_api.cpp")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
-# the projections call the vendor GEMM
-LINK_LIBS = ["-L" + os.path.join(ROCM, "lib"), "-lrocblas"]
+# the projections call the vendor GEMMs (rocBLAS, hipBLASLt for the fused bias)
+LINK_LIBS = ["-L" + os.path.join(ROCM, "lib"), "-lrocblas", "-lhipblaslt"]
 
 # Packed-fp32 VALU forms are kept out of every kernel on purpose.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

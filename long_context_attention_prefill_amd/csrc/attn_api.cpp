@@ -91,7 +91,7 @@ int check(const void *q, const void *k, const void *v, const void *out, const fl
 int run(const void *q, const void *k, const void *v, void *out, float *lse,
         const int32_t *cu_q, const int32_t *cu_k, int32_t n_seqs, int32_t n_q_heads,
         int32_t n_kv_heads, int32_t head_dim, int32_t dtype, int32_t mask_kind, int32_t window,
-        float scale, void *stream) {
+        float scale, void *stream, int32_t q_stride = 0, int32_t kv_stride = 0) {
   const bool bf16 = dtype == ATTN_BF16;
   const int bm = bf16 ? attn::rows_per_workgroup_bf16(head_dim)
                       : attn::rows_per_workgroup_f32(head_dim);
@@ -112,6 +112,8 @@ int run(const void *q, const void *k, const void *v, void *out, float *lse,
   a.lse = lse;
   a.hq = n_q_heads;
   a.hkv = n_kv_heads;
+  a.q_stride = q_stride > 0 ? q_stride : n_q_heads * head_dim;
+  a.kv_stride = kv_stride > 0 ? kv_stride : n_kv_heads * head_dim;
   a.group = n_q_heads / n_kv_heads;
   a.mask_kind = mask_kind;
   a.window = mask_kind == ATTN_WINDOW ? window : 0;
@@ -236,6 +238,23 @@ int check_decode(const void *q, const void *k, const void *v, const void *out, c
 }
 
 }  // namespace
+
+namespace attn {
+
+int prefill_strided(const void *q, const void *k, const void *v, void *out, float *lse,
+                    const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t n_seqs,
+                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                    int32_t mask_kind, int32_t window, float scale, int32_t q_stride,
+                    int32_t kv_stride, void *stream) {
+  if (q_stride < n_q_heads * head_dim || kv_stride < n_kv_heads * head_dim || q_stride % 8 != 0 ||
+      kv_stride % 8 != 0)
+    return ATTN_EINVAL;
+  if (n_seqs == 0 || cu_seqlens_q[n_seqs] == 0) return ATTN_OK;
+  return run(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, n_seqs, n_q_heads, n_kv_heads, head_dim, dtype,
+             mask_kind, window, scale, stream, q_stride, kv_stride);
+}
+
+}  // namespace attn
 
 extern "C" {
 

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const __bf16 *qrow = reinterpret_cast<const __bf16 *>(a.q) +
-                         ((size_t)(s0q + (row_ok[r] ? row[r] : 0)) * a.hq + h) * D;
+                         (size_t)(s0q + (row_ok[r] ? row[r] : 0)) * a.q_stride + (size_t)h * D;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk)
       qf[r][kk] = row_ok[r] && 16 * kk + 8 * g < D ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * kk + 8 * g)
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
 
   // Direct loads: wave-wide load j fills LDS slots 64j .. 64j+63 of a tile;
   // slot p is row p / SLOTS, chunk p % SLOTS (chunks >= CH are padding).
-  const int rowbytes = a.hkv * D * 2;  // bytes between consecutive tokens of one head
+  const int rowbytes = a.kv_stride * 2;  // bytes between consecutive tokens of one head
   uint32_t ld_off[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
@@ -229,8 +229,8 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
     const int rr = p / L::SLOTS, cs = p % L::SLOTS;
     ld_off[i] = cs < CH ? (uint32_t)(rr * rowbytes + cs * 16) : kOutOfRange;
   }
-  const char *kseq = reinterpret_cast<const char *>(a.k) + ((size_t)s0k * a.hkv + hk) * D * 2;
-  const char *vseq = reinterpret_cast<const char *>(a.v) + ((size_t)s0k * a.hkv + hk) * D * 2;
+  const char *kseq = reinterpret_cast<const char *>(a.k) + ((size_t)s0k * a.kv_stride + (size_t)hk * D) * 2;
+  const char *vseq = reinterpret_cast<const char *>(a.v) + ((size_t)s0k * a.kv_stride + (size_t)hk * D) * 2;
 
   // Direct loads of the K (or V) rows kt .. kt+63 into an LDS buffer.
   // kt >= kv_hi is allowed: the range is then empty, nothing is fetched and
@@ -665,8 +665,8 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_mfma(const LaunchArgs a) {
   // q[row][s + g D/2], s = 0 .. D/2 - 1
   float qv[H2];
   {
-    const float *qrow = reinterpret_cast<const float *>(a.q) +
-                        ((size_t)(s0q + (row_ok ? row : 0)) * a.hq + h) * D + g * H2;
+    const float *qrow = reinterpret_cast<const float *>(a.q) + (size_t)(s0q + (row_ok ? row : 0)) * a.q_stride +
+                        (size_t)h * D + g * H2;
 #pragma unroll
     for (int s4 = 0; s4 < H2; s4 += 4) {
       const f32x4 x = row_ok ? *reinterpret_cast<const f32x4 *>(qrow + s4) : (f32x4)(0.0f);
@@ -681,7 +681,7 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_mfma(const LaunchArgs a) {
     v_lds[1][D * VROW + i] = 0.0f;
   }
 
-  const size_t kv_rs = (size_t)a.hkv * D;
+  const size_t kv_rs = (size_t)a.kv_stride;
   const float *kbase = reinterpret_cast<const float *>(a.k) + (size_t)s0k * kv_rs + (size_t)hk * D;
   const float *vbase = reinterpret_cast<const float *>(a.v) + (size_t)s0k * kv_rs + (size_t)hk * D;
   // tile kt: thread loads float4 u = tid + 256 i of K and of V (key u / (D/4))

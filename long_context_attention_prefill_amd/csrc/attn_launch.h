@@ -28,6 +28,8 @@ struct LaunchArgs {
   float *lse;          // [Tq][hq] natural-log sum of exp(scale * score), or null
   int32_t hq;          // query heads
   int32_t hkv;         // key/value heads
+  int32_t q_stride;    // elements between consecutive tokens of q (hq * d when packed)
+  int32_t kv_stride;   // the same for k and v (hkv * d when packed); out is always packed
   int32_t group;       // hq / hkv
   int32_t mask_kind;   // MaskKind
   int32_t window;      // block length for kWindow
@@ -77,6 +79,17 @@ struct DecodeArgs {
   int32_t splits[kMaxDecodeSeqsPerLaunch];      // ceil(k_count / chunk)
   int32_t item_start[kMaxDecodeSeqsPerLaunch + 1];
 };
+
+// Prefill over q, k, v whose tokens lie q_stride and kv_stride elements
+// apart (heads still contiguous within a token; out packed), for callers
+// inside the library that hold q, k and v as column blocks of one
+// projection output.  Arguments as for attn_prefill_kv, checked by the
+// caller; returns an ATTN_ status.
+int prefill_strided(const void *q, const void *k, const void *v, void *out, float *lse,
+                    const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t n_seqs,
+                    int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                    int32_t mask_kind, int32_t window, float scale, int32_t q_stride,
+                    int32_t kv_stride, void *stream);
 
 // Kernel families.  Each returns 0 or a hipError_t value.
 int launch_bf16(const LaunchArgs &a, int head_dim, void *stream);

@@ -1,8 +1,11 @@
 // proj_api.cpp -- C ABI of the projections (include/proj.h): argument checks,
-// the dequantization launch and the vendor GEMM call (rocBLAS, bf16 in and
-// out, fp32 compute).  Host only.
+// the dequantization launch and the vendor GEMM calls (rocBLAS for the plain
+// product, hipBLASLt where the bias rides in the GEMM's epilogue; fp32
+// compute).  Host only.
 #include <cstdint>
+#include <vector>
 
+#include <hipblaslt/hipblaslt.h>
 #include <rocblas/rocblas.h>
 
 #include "proj.h"
@@ -28,25 +31,125 @@ rocblas_handle thread_handle() {
   return h;
 }
 
+// hipBLASLt plans of the biased product, per calling thread (handles and
+// descriptors are not shared between threads), created on first use of a
+// shape and kept for the life of the process; the bias pointer is set on
+// every call.
+struct LtPlan {
+  int64_t t, n, k;
+  bool f32;
+  bool ok;
+  hipblasLtMatmulDesc_t desc;
+  hipblasLtMatrixLayout_t la, lb, lc;
+  hipblasLtMatmulAlgo_t algo;
+};
+
+struct LtState {
+  hipblasLtHandle_t handle = nullptr;
+  std::vector<LtPlan> plans;
+};
+
+constexpr size_t kMaxLtPlans = 64;
+
+LtState *lt_state() {
+  thread_local LtState *st = nullptr;
+  if (st == nullptr) {
+    st = new LtState();
+    if (hipblasLtCreate(&st->handle) != HIPBLAS_STATUS_SUCCESS) st->handle = nullptr;
+  }
+  return st;
+}
+
+void lt_destroy(LtPlan &p) {
+  hipblasLtMatrixLayoutDestroy(p.la);
+  hipblasLtMatrixLayoutDestroy(p.lb);
+  hipblasLtMatrixLayoutDestroy(p.lc);
+  hipblasLtMatmulDescDestroy(p.desc);
+}
+
+// Row-major y[T][N] = x[T][K] w[N][K]^T + b is, column-major, the N x T matrix
+// op(W) X + b with W the K x N view of w (transposed), X the K x T view of x
+// and b broadcast along the T columns (the epilogue's bias runs along rows).
+const LtPlan *lt_plan(LtState *st, int64_t t, int64_t n, int64_t k, bool f32) {
+  for (const LtPlan &p : st->plans)
+    if (p.t == t && p.n == n && p.k == k && p.f32 == f32) return &p;
+  if (st->plans.size() >= kMaxLtPlans) {
+    lt_destroy(st->plans.front());
+    st->plans.erase(st->plans.begin());
+  }
+  LtPlan p{};
+  p.t = t;
+  p.n = n;
+  p.k = k;
+  p.f32 = f32;
+  const hipDataType dt = f32 ? HIP_R_32F : HIP_R_16BF;
+  bool good = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS;
+  const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+  const hipblasLtEpilogue_t ep = HIPBLASLT_EPILOGUE_BIAS;
+  const int32_t bias_type = dt;
+  good = good &&
+         hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) == HIPBLAS_STATUS_SUCCESS &&
+         hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) == HIPBLAS_STATUS_SUCCESS &&
+         hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_EPILOGUE, &ep, sizeof(ep)) == HIPBLAS_STATUS_SUCCESS &&
+         hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_BIAS_DATA_TYPE, &bias_type,
+                                         sizeof(bias_type)) == HIPBLAS_STATUS_SUCCESS;
+  good = good && hipblasLtMatrixLayoutCreate(&p.la, dt, k, n, k) == HIPBLAS_STATUS_SUCCESS &&
+         hipblasLtMatrixLayoutCreate(&p.lb, dt, k, t, k) == HIPBLAS_STATUS_SUCCESS &&
+         hipblasLtMatrixLayoutCreate(&p.lc, dt, n, t, n) == HIPBLAS_STATUS_SUCCESS;
+  if (good) {
+    // the heuristic's first choice, with no workspace: a fixed algorithm per
+    // shape, so repeated calls give the same bits
+    hipblasLtMatmulPreference_t pref = nullptr;
+    uint64_t ws = 0;
+    hipblasLtMatmulHeuristicResult_t res[1];
+    int found = 0;
+    good = hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
+           hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &ws, sizeof(ws)) ==
+               HIPBLAS_STATUS_SUCCESS &&
+           hipblasLtMatmulAlgoGetHeuristic(st->handle, p.desc, p.la, p.lb, p.lc, p.lc, pref, 1, res, &found) ==
+               HIPBLAS_STATUS_SUCCESS &&
+           found > 0;
+    if (pref != nullptr) hipblasLtMatmulPreferenceDestroy(pref);
+    if (good) p.algo = res[0].algo;
+  }
+  p.ok = good;
+  st->plans.push_back(p);
+  return &st->plans.back();
+}
+
 }  // namespace
 
 namespace proj {
 
-int gemm_nt(const void *x, const void *w, void *y, int64_t t, int64_t n, int64_t k, bool f32_in,
-            bool f32_out, void *stream) {
+int gemm_nt_bias(const void *x, const void *w, const void *bias, void *y, int64_t t, int64_t n, int64_t k,
+                 bool f32, void *stream) {
+  LtState *st = lt_state();
+  if (st->handle == nullptr) return -1;
+  const LtPlan *p = lt_plan(st, t, n, k, f32);
+  if (!p->ok) return -1;
+  if (hipblasLtMatmulDescSetAttribute(p->desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias)) !=
+      HIPBLAS_STATUS_SUCCESS)
+    return -1;
+  const float alpha = 1.0f, beta = 0.0f;
+  return hipblasLtMatmul(st->handle, p->desc, &alpha, w, p->la, x, p->lb, &beta, y, p->lc, y, p->lc, &p->algo,
+                         nullptr, 0, static_cast<hipStream_t>(stream)) == HIPBLAS_STATUS_SUCCESS
+             ? 0
+             : -1;
+}
+
+int gemm_nt(const void *x, const void *w, void *y, int64_t t, int64_t n, int64_t k, void *stream) {
   rocblas_handle h = thread_handle();
   if (h == nullptr) return -1;
   if (rocblas_set_stream(h, static_cast<hipStream_t>(stream)) != rocblas_status_success) return -1;
   // Row-major y[T][N] = x[T][K] w[N][K]^T is, column-major, the N x T matrix
   // W^T X with W the K x N view of w (ld K) and X the K x T view of x (ld K).
-  const rocblas_datatype in = f32_in ? rocblas_datatype_f32_r : rocblas_datatype_bf16_r;
-  const rocblas_datatype out = f32_out ? rocblas_datatype_f32_r : in;
   const float alpha = 1.0f, beta = 0.0f;
   const rocblas_status st = rocblas_gemm_ex(
       h, rocblas_operation_transpose, rocblas_operation_none, static_cast<rocblas_int>(n),
-      static_cast<rocblas_int>(t), static_cast<rocblas_int>(k), &alpha, w, in, static_cast<rocblas_int>(k), x, in,
-      static_cast<rocblas_int>(k), &beta, y, out, static_cast<rocblas_int>(n), y, out,
-      static_cast<rocblas_int>(n), rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+      static_cast<rocblas_int>(t), static_cast<rocblas_int>(k), &alpha, w, rocblas_datatype_bf16_r,
+      static_cast<rocblas_int>(k), x, rocblas_datatype_bf16_r, static_cast<rocblas_int>(k), &beta, y,
+      rocblas_datatype_bf16_r, static_cast<rocblas_int>(n), y, rocblas_datatype_bf16_r, static_cast<rocblas_int>(n),
+      rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
   return st == rocblas_status_success ? 0 : -1;
 }
 
@@ -75,7 +178,7 @@ int proj_linear(const void *x, const void *w, void *y, int64_t t, int64_t n, int
   const uint64_t xb = static_cast<uint64_t>(t) * k * 2, wb = static_cast<uint64_t>(n) * k * 2,
                  yb = static_cast<uint64_t>(t) * n * 2;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, w, wb)) return ATTN_EINVAL;
-  return proj::gemm_nt(x, w, y, t, n, k, false, false, stream) == 0 ? ATTN_OK : ATTN_ELAUNCH;
+  return proj::gemm_nt(x, w, y, t, n, k, stream) == 0 ? ATTN_OK : ATTN_ELAUNCH;
 }
 
 }  // extern "C"

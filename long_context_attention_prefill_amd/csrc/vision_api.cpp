@@ -1,13 +1,15 @@
 // vision_api.cpp -- C ABI of the vision attention block (include/vision_block.h):
-// argument checks, workspace carving and the five stream-ordered steps
-// (QKV GEMM, bias + head split, attention, output GEMM, bias + cast).  Host only.
+// argument checks, workspace carving and the three stream-ordered steps.
+// The QKV projection writes [q | k | v] rows of 3 H d values with the bias
+// added in the GEMM's epilogue; the attention reads q, k and v in place as
+// column blocks of those rows; the output projection adds its bias the same
+// way.  Host only.
 #include <algorithm>
-#include <cmath>
 #include <cstdint>
 
 #include "vision_block.h"
+#include "attn_launch.h"
 #include "proj_launch.h"
-#include "vision_launch.h"
 
 namespace {
 
@@ -21,11 +23,11 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
 
 uint64_t round256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-// Workspace regions, each starting on a 256-byte boundary:
-//   f32  [T][max(3 H d, hidden)] fp32  -- the QKV GEMM's result, later the output GEMM's
-//   q, k, v, a [T][H][d] dtype         -- attention inputs and output
+// Workspace regions, each starting on a 256-byte boundary, both of the
+// block's dtype: qkv [T][3 H d] (the QKV projection with its bias) and
+// a [T][H d] (the attention output).
 struct Carve {
-  uint64_t f32_bytes, part_bytes, total;
+  uint64_t qkv_bytes, a_bytes, total;
 };
 
 int shape_ok(int32_t h, int32_t d, int32_t hidden, int32_t dtype) {
@@ -36,13 +38,13 @@ int shape_ok(int32_t h, int32_t d, int32_t hidden, int32_t dtype) {
   return ATTN_OK;
 }
 
-Carve carve(int64_t t, int32_t h, int32_t d, int32_t hidden, int32_t dtype) {
+Carve carve(int64_t t, int32_t h, int32_t d, int32_t dtype) {
   const uint64_t es = dtype == ATTN_F32 ? 4 : 2;
   const uint64_t hd = static_cast<uint64_t>(h) * d;
   Carve c;
-  c.f32_bytes = round256(static_cast<uint64_t>(t) * std::max<uint64_t>(3 * hd, hidden) * 4);
-  c.part_bytes = round256(static_cast<uint64_t>(t) * hd * es);
-  c.total = c.f32_bytes + 4 * c.part_bytes;
+  c.qkv_bytes = round256(static_cast<uint64_t>(t) * 3 * hd * es);
+  c.a_bytes = round256(static_cast<uint64_t>(t) * hd * es);
+  c.total = c.qkv_bytes + c.a_bytes;
   return c;
 }
 
@@ -56,7 +58,7 @@ int vision_attention_block_workspace_size(int64_t tokens, int32_t n_heads, int32
   const int rc = shape_ok(n_heads, head_dim, hidden, dtype);
   if (rc != ATTN_OK) return rc;
   if (tokens >= (int64_t(1) << 31)) return ATTN_EUNSUPPORTED;
-  *bytes = tokens == 0 ? 0 : carve(tokens, n_heads, head_dim, hidden, dtype).total;
+  *bytes = tokens == 0 ? 0 : carve(tokens, n_heads, head_dim, dtype).total;
   return ATTN_OK;
 }
 
@@ -77,9 +79,8 @@ int vision_attention_block(const void *x, const void *w_qkv, const void *b_qkv, 
   }
   if (T == 0) {
     // nothing to compute; the mask and scale must still be valid
-    rc = attn_prefill_check(nullptr, nullptr, nullptr, nullptr, cu_seqlens, n_seqs, n_heads, n_heads, head_dim,
-                            dtype, mask_kind, window, scale);
-    return rc;
+    return attn_prefill_check(nullptr, nullptr, nullptr, nullptr, cu_seqlens, n_seqs, n_heads, n_heads, head_dim,
+                              dtype, mask_kind, window, scale);
   }
   const void *ptrs[] = {x, w_qkv, b_qkv, w_o, b_o, out};
   for (const void *p : ptrs)
@@ -91,32 +92,28 @@ int vision_attention_block(const void *x, const void *w_qkv, const void *b_qkv, 
                             static_cast<uint64_t>(T) * hidden * es};
   for (int i = 0; i < 5; ++i)
     if (overlaps(out, bytes[5], ptrs[i], bytes[i])) return ATTN_EINVAL;
-  const Carve c = carve(T, n_heads, head_dim, hidden, dtype);
+  const Carve c = carve(T, n_heads, head_dim, dtype);
   if (workspace == nullptr || !aligned(workspace, 16) || workspace_bytes < c.total) return ATTN_EINVAL;
   for (int i = 0; i < 6; ++i)
     if (overlaps(workspace, c.total, ptrs[i], bytes[i])) return ATTN_EINVAL;
   char *ws = static_cast<char *>(workspace);
-  float *f32 = reinterpret_cast<float *>(ws);
-  void *q = ws + c.f32_bytes;
-  void *k = ws + c.f32_bytes + c.part_bytes;
-  void *v = ws + c.f32_bytes + 2 * c.part_bytes;
-  void *a = ws + c.f32_bytes + 3 * c.part_bytes;
+  char *qkv = ws;
+  void *a = ws + c.qkv_bytes;
+  const uint64_t block = hd * es;  // bytes of one of q, k, v within a qkv row
   // the attention's own checks (mask kind, window, scale, offsets) before any device work
-  rc = attn_prefill_check(q, k, v, a, cu_seqlens, n_seqs, n_heads, n_heads, head_dim, dtype, mask_kind, window,
-                          scale);
+  rc = attn_prefill_check(qkv, qkv + block, qkv + 2 * block, a, cu_seqlens, n_seqs, n_heads, n_heads, head_dim,
+                          dtype, mask_kind, window, scale);
   if (rc != ATTN_OK) return rc;
   if (T >= (int64_t(1) << 31)) return ATTN_EUNSUPPORTED;
-  const bool f32_in = dtype == ATTN_F32;
-  if (proj::gemm_nt(x, w_qkv, f32, T, static_cast<int64_t>(3 * hd), hidden, f32_in, true, stream) != 0)
+  const bool f32 = dtype == ATTN_F32;
+  if (proj::gemm_nt_bias(x, w_qkv, b_qkv, qkv, T, static_cast<int64_t>(3 * hd), hidden, f32, stream) != 0)
     return ATTN_ELAUNCH;
-  if (vision::launch_split_qkv(f32, b_qkv, q, k, v, T, static_cast<int32_t>(hd), f32_in, stream) != 0)
-    return ATTN_ELAUNCH;
-  rc = attn_prefill(q, k, v, a, cu_seqlens, n_seqs, n_heads, n_heads, head_dim, dtype, mask_kind, window, scale,
-                    stream);
+  rc = attn::prefill_strided(qkv, qkv + block, qkv + 2 * block, a, nullptr, cu_seqlens, cu_seqlens, n_seqs, n_heads,
+                             n_heads, head_dim, dtype, mask_kind, window, scale, static_cast<int32_t>(3 * hd),
+                             static_cast<int32_t>(3 * hd), stream);
   if (rc != ATTN_OK) return rc;
-  if (proj::gemm_nt(a, w_o, f32, T, hidden, static_cast<int64_t>(hd), f32_in, true, stream) != 0)
+  if (proj::gemm_nt_bias(a, w_o, b_o, out, T, hidden, static_cast<int64_t>(hd), f32, stream) != 0)
     return ATTN_ELAUNCH;
-  if (vision::launch_add_bias(f32, b_o, out, T, hidden, f32_in, stream) != 0) return ATTN_ELAUNCH;
   return ATTN_OK;
 }
 

@@ -38,7 +38,7 @@ def _r256(x):
     (5, 2, 64, 1024, lcap.ATTN_BF16, 2), (1, 1, 128, 8, lcap.ATTN_F32, 4),
 ])
 def test_workspace_size(T, H, d, hidden, dtype, es):
-    want = _r256(T * max(3 * H * d, hidden) * 4) + 4 * _r256(T * H * d * es)
+    want = _r256(T * 3 * H * d * es) + _r256(T * H * d * es)
     assert lcap.vision_attention_block_workspace_size(T, H, d, hidden, dtype) == want
     assert lcap.vision_attention_block_workspace_size(0, H, d, hidden, dtype) == 0
 
@@ -58,7 +58,7 @@ def test_workspace_size_rejects(lib, args, code):
 
 X, WQ, BQ, WO, BO, OUT, WS = (0x10000000 * i for i in range(1, 8))
 T, H, D, HID = 8, 2, 64, 128
-NEED = _r256(T * max(3 * H * D, HID) * 4) + 4 * _r256(T * H * D * 2)
+NEED = _r256(T * 3 * H * D * 2) + _r256(T * H * D * 2)
 BASE = dict(x=X, wq=WQ, bq=BQ, wo=WO, bo=BO, out=OUT, cu=[0, 3, 8], h=H, d=D, hidden=HID,
             dtype=lcap.ATTN_BF16, mask=lcap.ATTN_FULL, window=0, scale=0.125, ws=WS, ws_bytes=NEED)
 
