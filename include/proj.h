@@ -20,9 +20,10 @@
  *
  * Ownership and execution as for attn_prefill: the caller owns every buffer;
  * calls check all arguments on the host first, enqueue on `stream` and
- * return; status codes of attn_prefill.h.  proj_linear uses one rocBLAS handle
- * per calling thread, created on the thread's first call (rocBLAS keeps its own
- * device workspace with it).
+ * return; status codes of attn_prefill.h.  proj_linear calls hipBLASLt with
+ * one handle per calling thread and one plan per shape, created on first use
+ * (the heuristic's first algorithm, which needs no GEMM workspace, so a
+ * shape always runs the same algorithm and gives the same bits).
  */
 #ifndef PROJ_H
 #define PROJ_H
@@ -48,12 +49,13 @@ int proj_dequantize_int8(const int8_t *q, const float *scale, void *w, int64_t n
                          int64_t k, void *stream);
 
 /*
- * y = x w^T in bf16 with fp32 accumulation (vendor GEMM).
+ * y = x w^T in bf16 with fp32 accumulation (vendor GEMM, hipBLASLt).
  *   x  device bf16 [T][K];  w  device bf16 [N][K];  y  device bf16 [T][N],
  *   overlapping neither input.  T, N >= 0, K >= 1, each < 2^31.
  * Returns ATTN_OK (T * N = 0 does nothing), ATTN_EINVAL for NULL/misaligned
  * pointers, negative sizes, K < 1 or overlap, ATTN_EUNSUPPORTED for sizes of
- * 2^31 or more, ATTN_ELAUNCH when the vendor library fails.
+ * 2^31 or more, ATTN_ELAUNCH when the vendor library has no algorithm for
+ * the shape or fails.
  */
 int proj_linear(const void *x, const void *w, void *y, int64_t t, int64_t n, int64_t k,
                 void *stream);

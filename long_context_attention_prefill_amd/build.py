@@ -2,7 +2,7 @@
 
 Produces ``long_context_attention_prefill_amd/libattn_prefill.so`` for gfx950:
 the kernels (csrc/*.hip) compiled by hipcc, the host-only C ABI
-(csrc/*_api.cpp) compiled by g++, linked by hipcc against rocBLAS (the
+(csrc/*_api.cpp) compiled by g++, linked by hipcc against hipBLASLt (the
 vendor GEMM of the projections).
 """
 from __future__ import annotations
@@ -25,8 +25,8 @@ DEVICE_SOURCES = ("attn_fwd.hip", "attn_decode.hip", "gdn_fwd.hip", "proj_fwd.hi
 # Host-only sources (C ABI: checks and planning), compiled by g++.
 HOST_SOURCES = ("attn_api.cpp", "gdn_api.cpp", "proj_api.cpp", "vision_api.cpp")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
-# the projections call the vendor GEMMs (rocBLAS, hipBLASLt for the fused bias)
-LINK_LIBS = ["-L" + os.path.join(ROCM, "lib"), "-lrocblas", "-lhipblaslt"]
+# the projections call the vendor GEMM (hipBLASLt)
+LINK_LIBS = ["-L" + os.path.join(ROCM, "lib"), "-lhipblaslt"]
 
 # Packed-fp32 VALU forms are kept out of every kernel on purpose.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

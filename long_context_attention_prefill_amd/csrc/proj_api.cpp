@@ -1,12 +1,11 @@
 // proj_api.cpp -- C ABI of the projections (include/proj.h): argument checks,
-// the dequantization launch and the vendor GEMM calls (rocBLAS for the plain
-// product, hipBLASLt where the bias rides in the GEMM's epilogue; fp32
-// compute).  Host only.
+// the dequantization launch and the vendor GEMM calls (hipBLASLt, fp32
+// compute; a bias, when there is one, rides in the GEMM's epilogue).  Host
+// only.
 #include <cstdint>
 #include <vector>
 
 #include <hipblaslt/hipblaslt.h>
-#include <rocblas/rocblas.h>
 
 #include "proj.h"
 #include "proj_launch.h"
@@ -21,23 +20,14 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// One handle per calling thread: rocBLAS handles bind a stream and are not
-// meant to be shared between threads.  Created on first use, kept for the
-// life of the process (tearing it down at thread exit could race the HIP
-// runtime's own shutdown).
-rocblas_handle thread_handle() {
-  thread_local rocblas_handle h = nullptr;
-  if (h == nullptr && rocblas_create_handle(&h) != rocblas_status_success) h = nullptr;
-  return h;
-}
-
-// hipBLASLt plans of the biased product, per calling thread (handles and
-// descriptors are not shared between threads), created on first use of a
-// shape and kept for the life of the process; the bias pointer is set on
-// every call.
+// hipBLASLt plans, per calling thread (handles and descriptors are not
+// shared between threads), created on first use of a shape and kept for the
+// life of the process (tearing them down at thread exit could race the HIP
+// runtime's own shutdown); a biased plan gets its bias pointer on every call.
 struct LtPlan {
   int64_t t, n, k;
   bool f32;
+  bool bias;
   bool ok;
   hipblasLtMatmulDesc_t desc;
   hipblasLtMatrixLayout_t la, lb, lc;
@@ -67,12 +57,13 @@ void lt_destroy(LtPlan &p) {
   hipblasLtMatmulDescDestroy(p.desc);
 }
 
-// Row-major y[T][N] = x[T][K] w[N][K]^T + b is, column-major, the N x T matrix
-// op(W) X + b with W the K x N view of w (transposed), X the K x T view of x
-// and b broadcast along the T columns (the epilogue's bias runs along rows).
-const LtPlan *lt_plan(LtState *st, int64_t t, int64_t n, int64_t k, bool f32) {
+// Row-major y[T][N] = x[T][K] w[N][K]^T (+ b) is, column-major, the N x T
+// matrix op(W) X (+ b) with W the K x N view of w (transposed), X the K x T
+// view of x and b broadcast along the T columns (the epilogue's bias runs
+// along rows).
+const LtPlan *lt_plan(LtState *st, int64_t t, int64_t n, int64_t k, bool f32, bool bias) {
   for (const LtPlan &p : st->plans)
-    if (p.t == t && p.n == n && p.k == k && p.f32 == f32) return &p;
+    if (p.t == t && p.n == n && p.k == k && p.f32 == f32 && p.bias == bias) return &p;
   if (st->plans.size() >= kMaxLtPlans) {
     lt_destroy(st->plans.front());
     st->plans.erase(st->plans.begin());
@@ -82,17 +73,18 @@ const LtPlan *lt_plan(LtState *st, int64_t t, int64_t n, int64_t k, bool f32) {
   p.n = n;
   p.k = k;
   p.f32 = f32;
+  p.bias = bias;
   const hipDataType dt = f32 ? HIP_R_32F : HIP_R_16BF;
   bool good = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS;
   const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
-  const hipblasLtEpilogue_t ep = HIPBLASLT_EPILOGUE_BIAS;
+  const hipblasLtEpilogue_t ep = bias ? HIPBLASLT_EPILOGUE_BIAS : HIPBLASLT_EPILOGUE_DEFAULT;
   const int32_t bias_type = dt;
   good = good &&
          hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) == HIPBLAS_STATUS_SUCCESS &&
          hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) == HIPBLAS_STATUS_SUCCESS &&
          hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_EPILOGUE, &ep, sizeof(ep)) == HIPBLAS_STATUS_SUCCESS &&
-         hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_BIAS_DATA_TYPE, &bias_type,
-                                         sizeof(bias_type)) == HIPBLAS_STATUS_SUCCESS;
+         (!bias || hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_BIAS_DATA_TYPE, &bias_type,
+                                                   sizeof(bias_type)) == HIPBLAS_STATUS_SUCCESS);
   good = good && hipblasLtMatrixLayoutCreate(&p.la, dt, k, n, k) == HIPBLAS_STATUS_SUCCESS &&
          hipblasLtMatrixLayoutCreate(&p.lb, dt, k, t, k) == HIPBLAS_STATUS_SUCCESS &&
          hipblasLtMatrixLayoutCreate(&p.lc, dt, n, t, n) == HIPBLAS_STATUS_SUCCESS;
@@ -121,14 +113,17 @@ const LtPlan *lt_plan(LtState *st, int64_t t, int64_t n, int64_t k, bool f32) {
 
 namespace proj {
 
-int gemm_nt_bias(const void *x, const void *w, const void *bias, void *y, int64_t t, int64_t n, int64_t k,
-                 bool f32, void *stream) {
+namespace {
+
+int gemm(const void *x, const void *w, const void *bias, void *y, int64_t t, int64_t n, int64_t k, bool f32,
+         void *stream) {
   LtState *st = lt_state();
   if (st->handle == nullptr) return -1;
-  const LtPlan *p = lt_plan(st, t, n, k, f32);
+  const LtPlan *p = lt_plan(st, t, n, k, f32, bias != nullptr);
   if (!p->ok) return -1;
-  if (hipblasLtMatmulDescSetAttribute(p->desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias)) !=
-      HIPBLAS_STATUS_SUCCESS)
+  if (bias != nullptr &&
+      hipblasLtMatmulDescSetAttribute(p->desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias)) !=
+          HIPBLAS_STATUS_SUCCESS)
     return -1;
   const float alpha = 1.0f, beta = 0.0f;
   return hipblasLtMatmul(st->handle, p->desc, &alpha, w, p->la, x, p->lb, &beta, y, p->lc, y, p->lc, &p->algo,
@@ -137,20 +132,15 @@ int gemm_nt_bias(const void *x, const void *w, const void *bias, void *y, int64_
              : -1;
 }
 
+}  // namespace
+
 int gemm_nt(const void *x, const void *w, void *y, int64_t t, int64_t n, int64_t k, void *stream) {
-  rocblas_handle h = thread_handle();
-  if (h == nullptr) return -1;
-  if (rocblas_set_stream(h, static_cast<hipStream_t>(stream)) != rocblas_status_success) return -1;
-  // Row-major y[T][N] = x[T][K] w[N][K]^T is, column-major, the N x T matrix
-  // W^T X with W the K x N view of w (ld K) and X the K x T view of x (ld K).
-  const float alpha = 1.0f, beta = 0.0f;
-  const rocblas_status st = rocblas_gemm_ex(
-      h, rocblas_operation_transpose, rocblas_operation_none, static_cast<rocblas_int>(n),
-      static_cast<rocblas_int>(t), static_cast<rocblas_int>(k), &alpha, w, rocblas_datatype_bf16_r,
-      static_cast<rocblas_int>(k), x, rocblas_datatype_bf16_r, static_cast<rocblas_int>(k), &beta, y,
-      rocblas_datatype_bf16_r, static_cast<rocblas_int>(n), y, rocblas_datatype_bf16_r, static_cast<rocblas_int>(n),
-      rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-  return st == rocblas_status_success ? 0 : -1;
+  return gemm(x, w, nullptr, y, t, n, k, false, stream);
+}
+
+int gemm_nt_bias(const void *x, const void *w, const void *bias, void *y, int64_t t, int64_t n, int64_t k,
+                 bool f32, void *stream) {
+  return bias == nullptr ? -1 : gemm(x, w, bias, y, t, n, k, f32, stream);
 }
 
 }  // namespace proj

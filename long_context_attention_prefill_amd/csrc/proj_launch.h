@@ -11,9 +11,9 @@ namespace proj {
 int launch_dequantize_int8(const int8_t *q, const float *scale, void *w, int64_t n, int64_t k,
                            void *stream);
 
-// y[T][N] = x[T][K] w[N][K]^T by the vendor GEMM (rocBLAS), bf16 in and out,
-// fp32 accumulation.  Sizes already checked (each < 2^31, K >= 1).  Returns
-// 0 or -1.
+// y[T][N] = x[T][K] w[N][K]^T by the vendor GEMM (hipBLASLt), bf16 in and
+// out, fp32 accumulation.  Sizes already checked (each < 2^31, K >= 1).
+// Returns 0 or -1.
 int gemm_nt(const void *x, const void *w, void *y, int64_t t, int64_t n, int64_t k, void *stream);
 
 // y[T][N] = x[T][K] w[N][K]^T + b[N] by the vendor GEMM (hipBLASLt, the bias
