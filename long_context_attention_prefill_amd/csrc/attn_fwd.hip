@@ -309,8 +309,11 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
   // Schedule of a plain tile (one basic block): the MFMAs of the second
   // 32-key block of S^T run under the softmax of the first, and the PV MFMAs
   // of the first two k steps under the softmax of the second, with a few LDS
-  // reads kept ahead of their MFMAs and the next tile's loads spread over
-  // the first MFMAs (mask: 2 VALU, 8 MFMA, 0x20 VMEM read, 0x100 DS read).
+  // reads kept ahead of their MFMAs and the next tile's loads one per MFMA
+  // of the first block (any left over follow: issued in a burst, eight
+  // waves' loads back up the CU's load pipe and stall the MFMA issue; one
+  // per MFMA measured 0.7 % faster at 10k and 3-7 % at 1-2k tokens) (mask:
+  // 2 VALU, 8 MFMA, 0x20 VMEM read, 0x100 DS read).
   auto plain_tile_schedule = [&]() {
     constexpr int SOFT = 3 * (BN / 2) / KST;  // softmax VALU ops per QK MFMA
     constexpr int PV_HALF = DB * (BN / 32);   // PV k-step pairs' fragments
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
 #pragma unroll
     for (int i = 0; i < KST; ++i) {  // S^T block 0, with the next tile's loads
       __builtin_amdgcn_sched_group_barrier(0x008, R, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 2 * NL / KST + 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 #pragma unroll
