@@ -1,6 +1,7 @@
-"""vision_attention_block (QKV GEMM, HIP bias/split, HIP attention, output
-GEMM, HIP bias/cast) against the fp64 oracle, through the C ABI, on the same
-seeded inputs.
+"""vision_attention_block (QKV GEMM with the bias in its epilogue, the HIP
+attention kernels reading q, k, v in place from the QKV rows, output GEMM
+with its bias) against the fp64 oracle, through the C ABI, on the same seeded
+inputs.
 
 Tolerance.  bf16: the block rounds q, k and v once each to bf16, the
 attention rounds its probabilities and its output to bf16, and the result is
