@@ -199,3 +199,35 @@ def test_gdn_workloads_full_size(gdn_orc, name):
     want, want_fin = gdn_orc.gated_delta_rule(q, k, v, g, beta, cu, scale)
     _assert_close(got, want, "outputs")
     _assert_close(fin, want_fin, "final state")
+
+
+@pytest.mark.parametrize("lens", [[4096], [4100, 0, 70], [9000, 130]], ids=str)
+@pytest.mark.parametrize("with_s0", [False, True], ids=["zero_state", "initial_state"])
+def test_gdn_long_and_ragged(gdn_orc, lens, with_s0):
+    """Sequences of 64 to 141 chunks (one ending one token into a chunk),
+    packed with short and empty ones."""
+    _check(gdn_orc, lens, 2, seed=sum(lens) % 1000, with_s0=with_s0)
+
+
+def test_gdn_long_state_in_place(gdn_orc):
+    """A long sequence updating the state in place, then run without any state."""
+    import torch
+
+    import long_context_attention_prefill_amd as lcap
+
+    lens = [4200, 300]
+    cu = [0, 4200, 4500]
+    q, k, v, g, beta = W.make_gdn_inputs(lens, 2, 128, 128, 95)
+    s0 = _state0(2, 2, 96)
+    scale = 1 / math.sqrt(128)
+    want, want_fin = gdn_orc.gated_delta_rule(q, k, v, g, beta, cu, scale, initial_state=s0)
+    tq, tk, tv = _dev(q, "bf16"), _dev(k, "bf16"), _dev(v, "bf16")
+    tg, tb = _dev(g, "f32"), _dev(beta, "f32")
+    state = _dev(s0, "f32")
+    out = lcap.gdn_prefill(tq, tk, tv, tg, tb, cu, scale=scale, initial_state=state, final_state=state)[0]
+    torch.cuda.synchronize()
+    _assert_close(out.double().cpu().numpy(), want, "outputs")
+    _assert_close(state.double().cpu().numpy(), want_fin, "state in place")
+    want0, _ = gdn_orc.gated_delta_rule(q, k, v, g, beta, cu, scale)
+    got0, _ = _run(q, k, v, g, beta, cu, scale, want_state=False)
+    _assert_close(got0, want0, "outputs without states")
