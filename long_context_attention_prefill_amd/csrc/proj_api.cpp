@@ -20,10 +20,11 @@ bool overlaps(const void *a, uint64_t na, const void *b, uint64_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// hipBLASLt plans, per calling thread (handles and descriptors are not
-// shared between threads), created on first use of a shape and kept for the
-// life of the process (tearing them down at thread exit could race the HIP
-// runtime's own shutdown); a biased plan gets its bias pointer on every call.
+// hipBLASLt plans, per calling thread and device (handles and descriptors
+// are not shared between threads, and a handle and its algorithms belong to
+// one device), created on first use of a shape and kept for the life of the
+// process (tearing them down at thread exit could race the HIP runtime's own
+// shutdown); a biased plan gets its bias pointer on every call.
 struct LtPlan {
   int64_t t, n, k;
   bool f32;
@@ -35,6 +36,7 @@ struct LtPlan {
 };
 
 struct LtState {
+  int device = -1;
   hipblasLtHandle_t handle = nullptr;
   std::vector<LtPlan> plans;
 };
@@ -42,19 +44,23 @@ struct LtState {
 constexpr size_t kMaxLtPlans = 64;
 
 LtState *lt_state() {
-  thread_local LtState *st = nullptr;
-  if (st == nullptr) {
-    st = new LtState();
-    if (hipblasLtCreate(&st->handle) != HIPBLAS_STATUS_SUCCESS) st->handle = nullptr;
-  }
+  thread_local std::vector<LtState *> per_device;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  for (LtState *st : per_device)
+    if (st->device == dev) return st;
+  LtState *st = new LtState();
+  st->device = dev;
+  if (hipblasLtCreate(&st->handle) != HIPBLAS_STATUS_SUCCESS) st->handle = nullptr;
+  per_device.push_back(st);
   return st;
 }
 
 void lt_destroy(LtPlan &p) {
-  hipblasLtMatrixLayoutDestroy(p.la);
-  hipblasLtMatrixLayoutDestroy(p.lb);
-  hipblasLtMatrixLayoutDestroy(p.lc);
-  hipblasLtMatmulDescDestroy(p.desc);
+  if (p.la != nullptr) hipblasLtMatrixLayoutDestroy(p.la);
+  if (p.lb != nullptr) hipblasLtMatrixLayoutDestroy(p.lb);
+  if (p.lc != nullptr) hipblasLtMatrixLayoutDestroy(p.lc);
+  if (p.desc != nullptr) hipblasLtMatmulDescDestroy(p.desc);
 }
 
 // Row-major y[T][N] = x[T][K] w[N][K]^T (+ b) is, column-major, the N x T
@@ -118,7 +124,7 @@ namespace {
 int gemm(const void *x, const void *w, const void *bias, void *y, int64_t t, int64_t n, int64_t k, bool f32,
          void *stream) {
   LtState *st = lt_state();
-  if (st->handle == nullptr) return -1;
+  if (st == nullptr || st->handle == nullptr) return -1;
   const LtPlan *p = lt_plan(st, t, n, k, f32, bias != nullptr);
   if (!p->ok) return -1;
   if (bias != nullptr &&
