@@ -41,6 +41,7 @@ PEAK_F32_TFLOPS = 157.3  # MI355X dense fp32 (matrix cores and vector ALUs alike
 KERNEL_SRCS = [os.path.join(ROOT, "long_context_attention_prefill_amd", "csrc", f)
                for f in ("attn_fwd.hip", "attn_device.h", "attn_launch.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_d128_causal_n10240.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_d128_causal_n10240_counters.txt")
 
 
 def pairs_of(w):
@@ -350,20 +351,43 @@ def kernel_digest():
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when that summary is missing or was taken on other kernel source."""
+def read_profile_fields(path):
+    """The `key: value` lines of a committed rocprofv3 summary, or None when
+    it is missing or was taken on other kernel source."""
     try:
         fields = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     fields[k.strip()] = v.strip()
-        if fields.get("kernel_source_sha256_16") != kernel_digest():
+    except OSError:
+        return None
+    return fields if fields.get("kernel_source_sha256_16") == kernel_digest() else None
+
+
+def read_traffic():
+    """HBM bytes per launch of the headline kernel (calibrated FETCH_SIZE +
+    WRITE_SIZE), or None."""
+    fields = read_profile_fields(TRAFFIC_FILE)
+    try:
+        return None if fields is None else float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def read_counters():
+    """MFMA utilisation, VALU per MFMA, LDS bank conflicts and the shader clock
+    under load of the headline kernel (SQ / GRBM counters), or None."""
+    fields = read_profile_fields(COUNTERS_FILE)
+    try:
+        if fields is None:
             return None
-        return float(fields["hbm_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+        return {"mfma_busy_frac": float(fields["mfma_busy_frac"]),
+                "valu_per_mfma": float(fields["valu_per_mfma"]),
+                "lds_bank_conflicts": int(fields["lds_bank_conflicts"]),
+                "sclk_ghz_under_load": float(fields["sclk_ghz_under_load"])}
+    except (KeyError, ValueError):
         return None
 
 
@@ -493,6 +517,7 @@ def main():
         torch.cuda.synchronize()
 
     traffic = read_traffic()
+    counters = read_counters()
     line = {
         "metric": "attention prefill tokens/s (causal bf16, 10k tokens)",
         "value": round(w10.total_tokens / (ms10 * 1e-3), 1),
@@ -513,7 +538,7 @@ def main():
         "pct_bf16_peak": round(100 * tflops10 / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops10, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops10 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic,
+                     "traffic": traffic, "counters": counters,
                      "kernel": "fwd_bf16_fast<128,4,1>", "algorithmic_flops": flops10,
                      "algorithmic_bytes": bytes10},
     }
