@@ -326,7 +326,8 @@ struct ChunkRegs {
 //   waves 4..7  after U' is ready S^T[32(w-4) ..] <- Gam_last S^T + Kd U'.
 // Every wave also moves its share of the next chunk from registers into the
 // other LDS buffer and loads its share of the chunk after next, at the point
-// of the step where that costs its role least (waves 0, 1 after U').
+// of the step where that costs its role least (waves 0, 1 in the second
+// half, where they have no other work).
 constexpr int kScanWaves = 8;
 
 __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) {
@@ -465,11 +466,19 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
           for (int e = 0; e < 4; ++e) up[e] = (__bf16)((float)u4[e] - xy[4 * q4 + e]);
           *reinterpret_cast<bf16x4 *>(&upt[l32 * RT + t]) = up;
         }
+      } else {
+        store_chunk(buf ^ 1, ahead);
+        load_chunk(cn, fill);
       }
+    }
+    __syncthreads();  // U' ready; every read of sb done
+    if (x_wave) {
+      // the X waves, idle until the next chunk, move their share of it now
+      // (in the first half they delayed U', which everything waits for:
+      // measured 10 % slower)
       store_chunk(buf ^ 1, ahead);
       load_chunk(cn, fill);
     }
-    __syncthreads();  // U' ready; every read of sb done
 
     if (y_wave) {
       // O = diag(scale Gam) Q S^T + P U'
