@@ -91,7 +91,7 @@ int gdn_prefill(const void *q, const void *k, const void *v, const float *g,
                 uint64_t workspace_bytes, void *stream);
 
 /* Bytes of workspace gdn_prefill needs for this shape (host-only): per
- * 64-token chunk and head, 57600 bytes.  Returns the shape codes of
+ * 64-token chunk and head, 73984 bytes.  Returns the shape codes of
  * gdn_prefill. */
 int gdn_prefill_workspace_size(const int32_t *cu_seqlens, int32_t n_seqs,
                                int32_t n_heads, int32_t head_dim_k,

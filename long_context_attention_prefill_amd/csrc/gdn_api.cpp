@@ -171,6 +171,7 @@ int gdn_prefill(const void *q, const void *k, const void *v, const float *g, con
     a.ws_p = base_ptr + it * (gdn::kWBytes + gdn::kUBytes);
     a.ws_kd = base_ptr + it * (gdn::kWBytes + gdn::kUBytes + gdn::kPBytes);
     a.ws_gam = reinterpret_cast<float *>(base_ptr + it * (gdn::kWBytes + gdn::kUBytes + gdn::kPBytes + gdn::kKdBytes));
+    a.ws_q = base_ptr + it * (gdn::kWBytes + gdn::kUBytes + gdn::kPBytes + gdn::kKdBytes + gdn::kGamBytes);
     // without a final state, a launch of empty sequences has nothing to do
     if (items == 0 && final_state == nullptr) continue;
     plan.push_back(a);

@@ -63,6 +63,26 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 // Row of a 32 x 32 MFMA accumulator held in element e by a lane of half g.
 __device__ __forceinline__ int acc_row(int e, int g) { return 8 * (e >> 2) + 4 * g + (e & 3); }
 
+// Workspace order of element (r, c) of a row-major bf16 matrix with
+// 16 * ksteps columns: the order in which a wave reads it as the A (or B)
+// operand of 32 x 32 x 16 MFMAs -- 32-row blocks, then 16-column steps, then
+// the 64 lanes (lane = 32 * (8-column half) + row in the block), 8 columns per
+// lane -- so each 64-lane load of 16 bytes reads 1 KB of consecutive bytes.
+__device__ __forceinline__ int frag_index(int r, int c, int ksteps) {
+  return ((((r >> 5) * ksteps + (c >> 4)) * 64 + ((c >> 3) & 1) * 32 + (r & 31)) << 3) + (c & 7);
+}
+
+// Workspace order of U^T (value dim v, token t): what the scan's lane
+// (v % 32, half h) needs for U' = U - W S^T of the 32-token block holding t
+// is the accumulator rows 8j + 4h + i (j, i < 4) of that block, so per
+// (32-dim slice, token block) the lane's 16 tokens are two 16-byte loads, in
+// two halves of 64 lanes x 8.
+__device__ __forceinline__ int u_frag_index(int v, int t) {
+  const int tt = t & 31;
+  return (((((v >> 5) * 2 + (t >> 5)) * 2 + (tt >> 4)) * 64 + ((tt >> 2) & 1) * 32 + (v & 31)) << 3) +
+         ((tt >> 3) & 1) * 4 + (tt & 3);
+}
+
 // Launch-local chunk index -> sequence.
 __device__ __forceinline__ int seq_of_chunk(const GdnArgs &a, int cg) {
   int b = 0;
@@ -125,6 +145,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
   __bf16 *u_out = reinterpret_cast<__bf16 *>(a.ws_u) + (size_t)item * C * DV;
   __bf16 *p_out = reinterpret_cast<__bf16 *>(a.ws_p) + (size_t)item * C * C;
   __bf16 *kd_out = reinterpret_cast<__bf16 *>(a.ws_kd) + (size_t)item * DK * C;
+  __bf16 *q_out = reinterpret_cast<__bf16 *>(a.ws_q) + (size_t)item * C * DK;
   float *gam_out = a.ws_gam + (size_t)item * C;
 
   // K, Q, V rows of the chunk (rows past its end are zero), gates, betas
@@ -166,6 +187,14 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
   }
   __syncthreads();
 
+  // the queries again, in the scan's operand order: 16-byte piece pc of the
+  // copy is row 32 (pc >> 9) + (pc & 31), columns 16 ((pc >> 6) & 7) +
+  // 8 ((pc >> 5) & 1) .. +7 (frag_index)
+  for (int pc = tid; pc < C * DK / 8; pc += 256) {
+    const int r = 32 * (pc >> 9) + (pc & 31), c0 = 16 * ((pc >> 6) & 7) + 8 * ((pc >> 5) & 1);
+    *reinterpret_cast<bf16x8 *>(q_out + 8 * pc) = *reinterpret_cast<const bf16x8 *>(ql + r * RB + c0);
+  }
+
   // K K^T and Q K^T: wave w -> 32 x 32 block (w >> 1, w & 1); block (0, 1)
   // lies above the diagonal, where both A and P are zero.
   {
@@ -188,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
       const int i = 32 * bi + acc_row(e, g);
       const float dec = i >= j ? exp2_fast(gam_s[i] - gj) : 0.0f;  // Gam_i / Gam_j <= 1 for i >= j
       af[i * RF4 + j] = i > j ? beta_s[i] * dec * kk[e] : 0.0f;
-      p_out[i * C + j] = (__bf16)(a.scale * dec * qk[e]);
+      p_out[frag_index(i, j, C / 16)] = (__bf16)(a.scale * dec * qk[e]);
     }
   }
   __syncthreads();  // Q is no longer read: its region takes T
@@ -269,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
     bf16x8 x;
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = (__bf16)(fd_s[m0 + e] * (float)kl[(m0 + e) * RB + k]);
-    *reinterpret_cast<bf16x8 *>(kd_out + k * C + m0) = x;
+    *reinterpret_cast<bf16x8 *>(kd_out + frag_index(k, m0, C / 16)) = x;
   }
   __syncthreads();
 
@@ -296,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) w_out[(32 * ib + acc_row(e, g)) * DK + col] = (__bf16)wacc[ib][e];
+      for (int e = 0; e < 16; ++e) w_out[frag_index(32 * ib + acc_row(e, g), col, DK / 16)] = (__bf16)wacc[ib][e];
     // U transposed, [v][t]: four consecutive tokens per store
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
@@ -305,45 +334,70 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
         bf16x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = (__bf16)uacc[ib][4 * q4 + e];
-        *reinterpret_cast<bf16x4 *>(u_out + col * C + 32 * ib + 8 * q4 + 4 * g) = x;
+        *reinterpret_cast<bf16x4 *>(u_out + u_frag_index(col, 32 * ib + 8 * q4 + 4 * g)) = x;
       }
   }
 }
 
-// Registers holding a thread's share of one chunk's workspace rows and
-// queries on their way to LDS (all 512 threads of gdn_scan take part).
-struct ChunkRegs {
-  bf16x8 w[2], q[2], kd[2], p, u;
+// Eight waves per workgroup (two per SIMD, so one hides the other's
+// latencies), each with one role per chunk step:
+//   waves 0, 1  X = W S^T for token block 32w .. (8 MFMAs), then U' = U - X
+//               into LDS: the chain the next chunk depends on
+//   waves 2, 3  Y^T = S Q^T for token block 32(w-2) .., then after U' is
+//               ready O^T = diag(scale Gam) Y^T + U'^T P^T and the output
+//               store (each lane holds four consecutive value dims of one
+//               token: 8-byte row pieces straight from the accumulator)
+//   waves 4..7  after U' is ready S^T[32(w-4) ..] <- Gam_last S^T + Kd U'.
+// Every workspace row of a chunk is an MFMA operand of exactly one wave, so
+// each wave loads its own operands from global memory straight into
+// registers, kDepth chunks ahead (a ring of register sets, the step loop
+// unrolled by kDepth so every set is named statically); LDS holds only what
+// waves exchange: the bf16 state S and U'.  Each role runs its own loop; all
+// of them pass the same barriers (one before the first chunk, two per chunk).
+constexpr int kScanWaves = 8;
+constexpr int kDepth = 3;
+
+struct XRegs {      // waves 0, 1: W rows of the token block, U^T pieces
+  bf16x8 w[DK / 16];
+  bf16x8 u[2];
+};
+struct YRegs {      // waves 2, 3: query rows and P rows of the token block, Gam
+  bf16x8 q[DK / 16];
+  bf16x8 p[C / 16];
   float gam;
 };
+struct SRegs {      // waves 4..7: Kd rows of the key block, Gam_last
+  bf16x8 kd[C / 16];
+  float glast;
+};
 
-// Eight waves per workgroup (two per SIMD, so one hides the other's
-// latencies), each with one role per chunk:
-//   waves 0, 1  X = W S^T for token block 32w .. (8 MFMAs), then U' = U - X;
-//               the chain the next chunk depends on
-//   waves 2, 3  Y = Q S^T for token block 32(w-2) .., then after U' is
-//               ready O = diag(scale Gam) Y + P U' and the output store
-//   waves 4..7  after U' is ready S^T[32(w-4) ..] <- Gam_last S^T + Kd U'.
-// Every wave also moves its share of the next chunk from registers into the
-// other LDS buffer and loads its share of the chunk after next, at the point
-// of the step where that costs its role least (waves 0, 1 in the second
-// half, where they have no other work).
-constexpr int kScanWaves = 8;
+// Runs step(c, r[c % kDepth]) for c = 0 .. nchunks-1.  The main loop takes
+// whole groups of kDepth chunks with no early exit, so at its head the loads
+// in flight are always the same (the register sets in issue order) and the
+// compiler waits for the oldest set only; the last nchunks % kDepth steps
+// follow in a guarded tail.
+template <typename R, typename F>
+__device__ __forceinline__ void run_chunks(int nchunks, R (&r)[kDepth], F &&step) {
+  int c = 0;
+  for (; c + kDepth <= nchunks; c += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) step(c + d, r[d]);
+  }
+#pragma unroll
+  for (int d = 0; d < kDepth - 1; ++d)
+    if (c + d < nchunks) step(c + d, r[d]);
+}
 
 __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 wl[2][C * RB];
-  __shared__ __attribute__((aligned(16))) __bf16 qsl[2][C * RB];
-  __shared__ __attribute__((aligned(16))) __bf16 pl[2][C * RT];
-  __shared__ __attribute__((aligned(16))) __bf16 kdl[2][DK * RT];
-  __shared__ __attribute__((aligned(16))) __bf16 ul[2][kSliceRows * RT];  // U^T rows [v][t]
-  __shared__ __attribute__((aligned(16))) float gl[2][C];
-  __shared__ __attribute__((aligned(16))) __bf16 sb[kSliceRows * RB];     // S rows [v][k], bf16
-  __shared__ __attribute__((aligned(16))) __bf16 upt[kSliceRows * RT];    // U'^T rows [v][t], bf16
-  __shared__ __attribute__((aligned(16))) __bf16 ost[2][32 * RU];         // output rows [t][v]
+  __shared__ __attribute__((aligned(16))) __bf16 sb[kSliceRows * RB];   // S rows [v][k], bf16
+  __shared__ __attribute__((aligned(16))) __bf16 upt[kSliceRows * RT];  // U'^T rows [v][t], bf16
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform, and known to be: the roles below are then plain branches,
+  // not one exec-masked path through all three (whose loads the compiler
+  // would then wait for in every role)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
@@ -364,189 +418,179 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
   const int seq0 = a.seq_start[b];
   const int v0 = kSliceRows * s;
   const size_t state_off = ((size_t)(a.seq_base + b) * a.h + h) * DV * DK;
+  const int tb = 32 * (wave & 1);  // token block of X / Y / O
+  auto item_of = [&](int c) { return (size_t)(a.chunk_start[b] + c) * a.h + h; };
 
-  const bool x_wave = wave < 2, y_wave = wave >= 2 && wave < 4, s_wave = wave >= 4;
-  const int tb = 32 * (wave & 1);   // token block of X / Y / O
-  const int kb = 32 * (wave - 4);   // key rows of the state (state waves)
-
-  // State waves: S^T[kb + row][v0 + l32].
-  f32x16 st = (f32x16)(0.0f);
-  if (s_wave && a.s0 != nullptr) {
+  // B operand of X and A operand of Y^T: the bf16 state rows [v][k]
+  auto load_state_rows = [&](bf16x8 (&bv)[DK / 16]) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 x = *reinterpret_cast<const f32x4 *>(a.s0 + state_off + (size_t)(v0 + l32) * DK + kb +
-                                                       8 * q4 + 4 * g);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) st[4 * q4 + e] = x[e];
-    }
-  }
-
-  const __bf16 *Q = reinterpret_cast<const __bf16 *>(a.q);
-  auto load_chunk = [&](int c, ChunkRegs &r) {
-    const size_t item = (size_t)(a.chunk_start[b] + c) * a.h + h;
-    const __bf16 *w = reinterpret_cast<const __bf16 *>(a.ws_w) + item * C * DK;
-    const __bf16 *u = reinterpret_cast<const __bf16 *>(a.ws_u) + item * C * DV;
-    const __bf16 *p = reinterpret_cast<const __bf16 *>(a.ws_p) + item * C * C;
-    const __bf16 *kd = reinterpret_cast<const __bf16 *>(a.ws_kd) + item * DK * C;
-    const int t0 = seq0 + c * C;
-    const int n = min(C, seq_len - c * C);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 512 * i;
-      const int row = idx >> 4, cc = idx & 15;
-      r.w[i] = *reinterpret_cast<const bf16x8 *>(w + row * DK + cc * 8);
-      // rows past the chunk repeat its last token: they only feed output
-      // rows that are never stored (no select, so nothing waits on the load)
-      r.q[i] = *reinterpret_cast<const bf16x8 *>(Q + ((size_t)(t0 + min(row, n - 1)) * a.h + h) * DK + cc * 8);
-      r.kd[i] = *reinterpret_cast<const bf16x8 *>(kd + (idx >> 3) * C + (idx & 7) * 8);
-    }
-    r.p = *reinterpret_cast<const bf16x8 *>(p + (tid >> 3) * C + (tid & 7) * 8);
-    // the U slice is 256 pieces: both halves of the workgroup load it
-    r.u = *reinterpret_cast<const bf16x8 *>(u + (v0 + ((tid & 255) >> 3)) * C + (tid & 7) * 8);
-    r.gam = a.ws_gam[item * C + (tid & (C - 1))];
+    for (int ks = 0; ks < DK / 16; ++ks)
+      bv[ks] = *reinterpret_cast<const bf16x8 *>(&sb[l32 * RB + 16 * ks + 8 * g]);
   };
-  auto store_chunk = [&](int buf, const ChunkRegs &r) {
+  // A or B operand over the chunk's tokens: U'^T rows [v][t]
+  auto load_upt = [&](bf16x8 (&bu)[C / 16]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 512 * i;
-      const int row = idx >> 4, cc = idx & 15;
-      *reinterpret_cast<bf16x8 *>(&wl[buf][row * RB + cc * 8]) = r.w[i];
-      *reinterpret_cast<bf16x8 *>(&qsl[buf][row * RB + cc * 8]) = r.q[i];
-      *reinterpret_cast<bf16x8 *>(&kdl[buf][(idx >> 3) * RT + (idx & 7) * 8]) = r.kd[i];
-    }
-    *reinterpret_cast<bf16x8 *>(&pl[buf][(tid >> 3) * RT + (tid & 7) * 8]) = r.p;
-    if (tid < 256) *reinterpret_cast<bf16x8 *>(&ul[buf][(tid >> 3) * RT + (tid & 7) * 8]) = r.u;
-    if (tid < C) gl[buf][tid] = r.gam;
-  };
-  // state waves: bf16 copy of the state as S rows [v][k]
-  auto store_state = [&]() {
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      bf16x4 x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = (__bf16)st[4 * q4 + e];
-      *reinterpret_cast<bf16x4 *>(&sb[l32 * RB + kb + 8 * q4 + 4 * g]) = x;
-    }
+    for (int ks = 0; ks < C / 16; ++ks)
+      bu[ks] = *reinterpret_cast<const bf16x8 *>(&upt[l32 * RT + 16 * ks + 8 * g]);
   };
 
-  // One chunk step: chunk c computes from LDS buffer c & 1 while every wave
-  // writes its share of chunk c + 1 (held in `ahead`) into the other buffer
-  // (its last readers, chunk c - 1's, finished before this step began) and
-  // loads its share of chunk c + 2 into `fill` -- unconditionally (past the
-  // end: the last chunk again, never used), so the compiler counts the
-  // loads in flight exactly.
-  auto step = [&](int c, ChunkRegs &ahead, ChunkRegs &fill) __attribute__((always_inline)) {
-    const int buf = c & 1;
-    const int t0 = seq0 + c * C;
-    const int n = min(C, seq_len - c * C);
-    const int cn = min(c + 2, nchunks - 1);
-    f32x16 xy = (f32x16)(0.0f);
-    if (s_wave) {
-      store_chunk(buf ^ 1, ahead);
-      load_chunk(cn, fill);
-    } else {
-      // X = W S^T (waves 0, 1) or Y = Q S^T (waves 2, 3) for token block tb
-      const __bf16 *arow = (x_wave ? wl[buf] : qsl[buf]) + (tb + l32) * RB + 8 * g;
-      bf16x8 av[DK / 16], bv[DK / 16];
+  if (wave < 2) {
+    // ---- X waves: U' = U - W S^T ----
+    auto load = [&](int c, XRegs &r) {
+      const size_t item = item_of(c);
+      // (frag_index and u_frag_index: this lane's pieces are 1 KB apart)
+      const __bf16 *w = reinterpret_cast<const __bf16 *>(a.ws_w) + item * C * DK + frag_index(tb, 8 * g, DK / 16) + 8 * l32;
+      const __bf16 *u = reinterpret_cast<const __bf16 *>(a.ws_u) + item * C * DV + u_frag_index(v0 + l32, tb + 4 * g);
 #pragma unroll
-      for (int ks = 0; ks < DK / 16; ++ks) {
-        av[ks] = *reinterpret_cast<const bf16x8 *>(arow + 16 * ks);
-        bv[ks] = *reinterpret_cast<const bf16x8 *>(&sb[l32 * RB + 16 * ks + 8 * g]);
+      for (int j2 = 0; j2 < 2; ++j2) r.u[j2] = *reinterpret_cast<const bf16x8 *>(u + 512 * j2);
+#pragma unroll
+      for (int ks = 0; ks < DK / 16; ++ks) r.w[ks] = *reinterpret_cast<const bf16x8 *>(w + 512 * ks);
+    };
+    auto step = [&](int c, XRegs &r) __attribute__((always_inline)) {
+      bf16x8 bv[DK / 16];
+      load_state_rows(bv);
+      f32x16 x = (f32x16)(0.0f);
+#pragma unroll
+      for (int ks = 0; ks < DK / 16; ++ks) x = mfma(r.w[ks], bv[ks], x);
+      // U' = U - X, stored transposed [v][t] in bf16
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 up;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) up[e] = (__bf16)((float)r.u[j >> 1][4 * (j & 1) + e] - x[4 * j + e]);
+        *reinterpret_cast<bf16x4 *>(&upt[l32 * RT + tb + 8 * j + 4 * g]) = up;
       }
+      // operands of the chunk kDepth ahead (past the end: the last chunk
+      // again, never used; unconditional, so the loads in flight are counted
+      // exactly)
+      load(min(c + kDepth, nchunks - 1), r);
+      __syncthreads();  // U' ready; every read of sb done
+      __syncthreads();  // the new state ready
+    };
+    XRegs r[kDepth];
+    if (nchunks > 0) {
 #pragma unroll
-      for (int ks = 0; ks < DK / 16; ++ks) xy = mfma(av[ks], bv[ks], xy);
-      if (x_wave) {
-        // U' = U - X, stored transposed [v][t] in bf16
+      for (int d = 0; d < kDepth; ++d) load(min(d, nchunks - 1), r[d]);
+    }
+    __syncthreads();  // initial state in sb
+    run_chunks(nchunks, r, step);
+  } else if (wave < 4) {
+    // ---- Y waves: O^T = diag(scale Gam) S Q^T + U'^T P^T ----
+    auto load_q = [&](int c, YRegs &r) {
+      // the prep's copy of the chunk's queries (rows past its end are zero:
+      // they only feed output columns that are never stored)
+      const __bf16 *q = reinterpret_cast<const __bf16 *>(a.ws_q) + item_of(c) * C * DK + frag_index(tb, 8 * g, DK / 16) + 8 * l32;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int t = tb + 8 * q4 + 4 * g;
-          const bf16x4 u4 = *reinterpret_cast<const bf16x4 *>(&ul[buf][l32 * RT + t]);
-          bf16x4 up;
+      for (int ks = 0; ks < DK / 16; ++ks) r.q[ks] = *reinterpret_cast<const bf16x8 *>(q + 512 * ks);
+    };
+    auto load_p = [&](int c, YRegs &r) {
+      const size_t item = item_of(c);
+      const __bf16 *p = reinterpret_cast<const __bf16 *>(a.ws_p) + item * C * C + frag_index(tb, 8 * g, C / 16) + 8 * l32;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) up[e] = (__bf16)((float)u4[e] - xy[4 * q4 + e]);
-          *reinterpret_cast<bf16x4 *>(&upt[l32 * RT + t]) = up;
+      for (int ks = 0; ks < C / 16; ++ks) r.p[ks] = *reinterpret_cast<const bf16x8 *>(p + 512 * ks);
+      r.gam = a.ws_gam[item * C + tb + l32];
+    };
+    __bf16 *orow = reinterpret_cast<__bf16 *>(a.out);
+    auto step = [&](int c, YRegs &r) __attribute__((always_inline)) {
+      const int cn = min(c + kDepth, nchunks - 1);
+      bf16x8 bv[DK / 16];
+      load_state_rows(bv);
+      f32x16 y = (f32x16)(0.0f);
+#pragma unroll
+      for (int ks = 0; ks < DK / 16; ++ks) y = mfma(bv[ks], r.q[ks], y);
+      load_q(cn, r);
+      __syncthreads();  // U' ready; every read of sb done
+      const float sg = a.scale * r.gam;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) y[e] *= sg;
+      bf16x8 bu[C / 16];
+      load_upt(bu);
+#pragma unroll
+      for (int ks = 0; ks < C / 16; ++ks) y = mfma(bu[ks], r.p[ks], y);
+      load_p(cn, r);
+      // lane: token tb + l32, value dims v0 + 8j + 4g .. +3
+      const int t0 = seq0 + c * C;
+      const int n = min(C, seq_len - c * C);
+      if (tb + l32 < n) {
+        __bf16 *o = orow + ((size_t)(t0 + tb + l32) * a.h + h) * DV + v0 + 4 * g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = (__bf16)y[4 * j + e];
+          *reinterpret_cast<bf16x4 *>(o + 8 * j) = x;
         }
-      } else {
-        store_chunk(buf ^ 1, ahead);
-        load_chunk(cn, fill);
+      }
+      __syncthreads();  // the new state ready
+    };
+    YRegs r[kDepth];
+    if (nchunks > 0) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        load_q(min(d, nchunks - 1), r[d]);
+        load_p(min(d, nchunks - 1), r[d]);
       }
     }
-    __syncthreads();  // U' ready; every read of sb done
-    if (x_wave) {
-      // the X waves, idle until the next chunk, move their share of it now
-      // (in the first half they delayed U', which everything waits for:
-      // measured 10 % slower)
-      store_chunk(buf ^ 1, ahead);
-      load_chunk(cn, fill);
-    }
-
-    if (y_wave) {
-      // O = diag(scale Gam) Q S^T + P U'
+    __syncthreads();  // initial state in sb
+    run_chunks(nchunks, r, step);
+  } else {
+    // ---- state waves: S^T[kb ..] <- Gam_last S^T + Kd U' ----
+    const int kb = 32 * (wave - 4);  // key rows of the state
+    f32x16 st = (f32x16)(0.0f);      // S^T[kb + row][v0 + l32]
+    if (a.s0 != nullptr) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 gm = *reinterpret_cast<const f32x4 *>(&gl[buf][tb + 8 * q4 + 4 * g]);
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(a.s0 + state_off + (size_t)(v0 + l32) * DK + kb +
+                                                         8 * q4 + 4 * g);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) xy[4 * q4 + e] *= a.scale * gm[e];
+        for (int e = 0; e < 4; ++e) st[4 * q4 + e] = x[e];
       }
-      bf16x8 ap[C / 16], bu[C / 16];
-#pragma unroll
-      for (int ks = 0; ks < C / 16; ++ks) {
-        ap[ks] = *reinterpret_cast<const bf16x8 *>(&pl[buf][(tb + l32) * RT + 16 * ks + 8 * g]);
-        bu[ks] = *reinterpret_cast<const bf16x8 *>(&upt[l32 * RT + 16 * ks + 8 * g]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < C / 16; ++ks) xy = mfma(ap[ks], bu[ks], xy);
-      // through this wave's LDS tile to 16-byte row stores
-      __bf16 *os = ost[wave - 2];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) os[acc_row(e, g) * RU + l32] = (__bf16)xy[e];
-      __bf16 *orow = reinterpret_cast<__bf16 *>(a.out);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int j = lane + 64 * i;
-        const int t = j >> 2, cq = j & 3;
-        const bf16x8 ov = *reinterpret_cast<const bf16x8 *>(os + t * RU + 8 * cq);
-        if (tb + t < n)
-          *reinterpret_cast<bf16x8 *>(orow + ((size_t)(t0 + tb + t) * a.h + h) * DV + v0 + 8 * cq) = ov;
-      }
-    } else if (s_wave) {
-      // S^T <- Gam_last S^T + Kd U'
-      const float glast = gl[buf][C - 1];
-      bf16x8 ak[C / 16], bu[C / 16];
-#pragma unroll
-      for (int ks = 0; ks < C / 16; ++ks) {
-        ak[ks] = *reinterpret_cast<const bf16x8 *>(&kdl[buf][(kb + l32) * RT + 16 * ks + 8 * g]);
-        bu[ks] = *reinterpret_cast<const bf16x8 *>(&upt[l32 * RT + 16 * ks + 8 * g]);
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) st[e] *= glast;
-#pragma unroll
-      for (int ks = 0; ks < C / 16; ++ks) st = mfma(ak[ks], bu[ks], st);
-      store_state();
     }
-    __syncthreads();  // next chunk's rows and the new state ready
-  };
-
-  ChunkRegs ra, rb;
-  if (nchunks > 0) {
-    load_chunk(0, ra);
-    store_chunk(0, ra);
-    load_chunk(min(1, nchunks - 1), rb);
-  }
-  if (s_wave) store_state();
-  __syncthreads();
-  for (int c = 0; c < nchunks; c += 2) {
-    step(c, rb, ra);
-    if (c + 1 < nchunks) step(c + 1, ra, rb);
-  }
-
-  if (s_wave && a.s_final != nullptr) {
+    // bf16 copy of the state as S rows [v][k]
+    auto store_state = [&]() {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      f32x4 x;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 x;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = st[4 * q4 + e];
-      *reinterpret_cast<f32x4 *>(a.s_final + state_off + (size_t)(v0 + l32) * DK + kb + 8 * q4 + 4 * g) = x;
+        for (int e = 0; e < 4; ++e) x[e] = (__bf16)st[4 * q4 + e];
+        *reinterpret_cast<bf16x4 *>(&sb[l32 * RB + kb + 8 * q4 + 4 * g]) = x;
+      }
+    };
+    auto load = [&](int c, SRegs &r) {
+      const size_t item = item_of(c);
+      const __bf16 *kd = reinterpret_cast<const __bf16 *>(a.ws_kd) + item * DK * C + frag_index(kb, 8 * g, C / 16) + 8 * l32;
+#pragma unroll
+      for (int ks = 0; ks < C / 16; ++ks) r.kd[ks] = *reinterpret_cast<const bf16x8 *>(kd + 512 * ks);
+      r.glast = a.ws_gam[item * C + C - 1];
+    };
+    auto step = [&](int c, SRegs &r) __attribute__((always_inline)) {
+      __syncthreads();  // U' ready; every read of sb done
+      bf16x8 bu[C / 16];
+      load_upt(bu);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st[e] *= r.glast;
+#pragma unroll
+      for (int ks = 0; ks < C / 16; ++ks) st = mfma(r.kd[ks], bu[ks], st);
+      load(min(c + kDepth, nchunks - 1), r);
+      store_state();
+      __syncthreads();  // the new state ready
+    };
+    store_state();
+    SRegs r[kDepth];
+    if (nchunks > 0) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) load(min(d, nchunks - 1), r[d]);
+    }
+    __syncthreads();  // initial state in sb
+    run_chunks(nchunks, r, step);
+    if (a.s_final != nullptr) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = st[4 * q4 + e];
+        *reinterpret_cast<f32x4 *>(a.s_final + state_off + (size_t)(v0 + l32) * DK + kb + 8 * q4 + 4 * g) = x;
+      }
     }
   }
 }

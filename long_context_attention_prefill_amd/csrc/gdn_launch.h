@@ -13,7 +13,7 @@ constexpr int kChunk = 64;              // tokens per chunk
 constexpr int kMaxSeqsPerLaunch = 64;   // longer batches: several launches in order
 constexpr int kDk = 128;
 constexpr int kDv = 128;
-constexpr int kSliceRows = 32;          // value dims per MFMA block of the state (a scan workgroup takes two)
+constexpr int kSliceRows = 32;          // value dims of the state per scan workgroup
 
 // Workspace per (chunk, head) item, each array item-major:
 //   w    bf16 [64][128]  T diag(beta Gamma) K       (WY key combinations)
@@ -21,12 +21,17 @@ constexpr int kSliceRows = 32;          // value dims per MFMA block of the stat
 //   p    bf16 [64][64]   scale (Q K^T o M), M_ij = Gamma_i / Gamma_j (i >= j)
 //   kd   bf16 [128][64]  K^T diag(Gamma_last / Gamma)  (transposed)
 //   gam  f32  [64]       Gamma_i = exp(cumulative g within the chunk)
+//   q    bf16 [64][128]  the chunk's queries (rows past its end zero)
+// The bf16 matrices are stored in the order the scan's waves read them as
+// MFMA operands (gdn_fwd.hip, frag_index and u_frag_index), so each 64-lane
+// load of the scan reads 1 KB of consecutive bytes.
 constexpr uint64_t kWBytes = kChunk * kDk * 2;
 constexpr uint64_t kUBytes = kChunk * kDv * 2;
 constexpr uint64_t kPBytes = kChunk * kChunk * 2;
 constexpr uint64_t kKdBytes = kDk * kChunk * 2;
 constexpr uint64_t kGamBytes = kChunk * 4;
-constexpr uint64_t kItemBytes = kWBytes + kUBytes + kPBytes + kKdBytes + kGamBytes;
+constexpr uint64_t kQBytes = kChunk * kDk * 2;
+constexpr uint64_t kItemBytes = kWBytes + kUBytes + kPBytes + kKdBytes + kGamBytes + kQBytes;
 
 struct GdnArgs {
   const void *q;            // [T][H][128] bf16
@@ -42,6 +47,7 @@ struct GdnArgs {
   void *ws_p;
   void *ws_kd;
   float *ws_gam;
+  void *ws_q;
   int32_t h;                // heads
   float scale;
   int32_t n_seqs;           // sequences in this launch

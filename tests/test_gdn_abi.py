@@ -11,7 +11,7 @@ import long_context_attention_prefill_amd as lcap
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn_prefill.h")
 
-ITEM_BYTES = 57600  # per 64-token chunk and head, as the header states
+ITEM_BYTES = 73984  # per 64-token chunk and head, as the header states
 
 
 @pytest.fixture(scope="module")
