@@ -350,8 +350,10 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
 //   waves 4..7  after U' is ready S^T[32(w-4) ..] <- Gam_last S^T + Kd U'.
 // Every workspace row of a chunk is an MFMA operand of exactly one wave, so
 // each wave loads its own operands from global memory straight into
-// registers, kDepth chunks ahead (a ring of register sets, the step loop
-// unrolled by kDepth so every set is named statically); LDS holds only what
+// registers, in the half of the step where its role leaves it idle: kDepth
+// chunks ahead for waves 0..3, kDepth - 1 for the state waves (a ring of
+// register sets, the step loop unrolled by kDepth so every set is named
+// statically); LDS holds only what
 // waves exchange: the bf16 state S and U'.  Each role runs its own loop; all
 // of them pass the same barriers (one before the first chunk, two per chunk).
 constexpr int kScanWaves = 8;
@@ -371,22 +373,30 @@ struct SRegs {      // waves 4..7: Kd rows of the key block, Gam_last
   float glast;
 };
 
-// Runs step(c, r[c % kDepth]) for c = 0 .. nchunks-1.  The main loop takes
-// whole groups of kDepth chunks with no early exit, so at its head the loads
-// in flight are always the same (the register sets in issue order) and the
-// compiler waits for the oldest set only; the last nchunks % kDepth steps
-// follow in a guarded tail.
+// Runs step(c, r[c % kDepth], r[(c - 1) % kDepth]) for c = 0 .. nchunks-1:
+// the set holding chunk c, and the one chunk c - 1 used (free again).  The
+// main loop takes whole groups of kDepth chunks with no early exit, so at
+// its head the loads in flight are always the same (the register sets in
+// issue order) and the compiler waits for the oldest set only; the last
+// nchunks % kDepth steps follow in a guarded tail.
 template <typename R, typename F>
 __device__ __forceinline__ void run_chunks(int nchunks, R (&r)[kDepth], F &&step) {
   int c = 0;
   for (; c + kDepth <= nchunks; c += kDepth) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) step(c + d, r[d]);
+    for (int d = 0; d < kDepth; ++d) step(c + d, r[d], r[(d + kDepth - 1) % kDepth]);
   }
 #pragma unroll
   for (int d = 0; d < kDepth - 1; ++d)
-    if (c + d < nchunks) step(c + d, r[d]);
+    if (c + d < nchunks) step(c + d, r[d], r[(d + kDepth - 1) % kDepth]);
 }
+
+// The compiler chains the three role branches through shared join blocks,
+// so loads a role leaves in flight when it ends would count, for its wait
+// counts, against the next role's loop.  Each role ends with none in flight
+// (its last loads are operands past the end, never used), which costs
+// nothing: the wave has no work left.
+__device__ __forceinline__ void drain_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 
 __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 sb[kSliceRows * RB];   // S rows [v][k], bf16
@@ -446,7 +456,7 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
 #pragma unroll
       for (int ks = 0; ks < DK / 16; ++ks) r.w[ks] = *reinterpret_cast<const bf16x8 *>(w + 512 * ks);
     };
-    auto step = [&](int c, XRegs &r) __attribute__((always_inline)) {
+    auto step = [&](int c, XRegs &r, XRegs &) __attribute__((always_inline)) {
       bf16x8 bv[DK / 16];
       load_state_rows(bv);
       f32x16 x = (f32x16)(0.0f);
@@ -460,11 +470,12 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
         for (int e = 0; e < 4; ++e) up[e] = (__bf16)((float)r.u[j >> 1][4 * (j & 1) + e] - x[4 * j + e]);
         *reinterpret_cast<bf16x4 *>(&upt[l32 * RT + tb + 8 * j + 4 * g]) = up;
       }
-      // operands of the chunk kDepth ahead (past the end: the last chunk
+      __syncthreads();  // U' ready; every read of sb done
+      // operands of the chunk kDepth ahead, in the half of the step where
+      // this wave has nothing else to do (past the end: the last chunk
       // again, never used; unconditional, so the loads in flight are counted
       // exactly)
       load(min(c + kDepth, nchunks - 1), r);
-      __syncthreads();  // U' ready; every read of sb done
       __syncthreads();  // the new state ready
     };
     XRegs r[kDepth];
@@ -474,6 +485,7 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
     }
     __syncthreads();  // initial state in sb
     run_chunks(nchunks, r, step);
+    drain_loads();
   } else if (wave < 4) {
     // ---- Y waves: O^T = diag(scale Gam) S Q^T + U'^T P^T ----
     auto load_q = [&](int c, YRegs &r) {
@@ -491,7 +503,7 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
       r.gam = a.ws_gam[item * C + tb + l32];
     };
     __bf16 *orow = reinterpret_cast<__bf16 *>(a.out);
-    auto step = [&](int c, YRegs &r) __attribute__((always_inline)) {
+    auto step = [&](int c, YRegs &r, YRegs &) __attribute__((always_inline)) {
       const int cn = min(c + kDepth, nchunks - 1);
       bf16x8 bv[DK / 16];
       load_state_rows(bv);
@@ -533,6 +545,7 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
     }
     __syncthreads();  // initial state in sb
     run_chunks(nchunks, r, step);
+    drain_loads();
   } else {
     // ---- state waves: S^T[kb ..] <- Gam_last S^T + Kd U' ----
     const int kb = 32 * (wave - 4);  // key rows of the state
@@ -563,7 +576,10 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
       for (int ks = 0; ks < C / 16; ++ks) r.kd[ks] = *reinterpret_cast<const bf16x8 *>(kd + 512 * ks);
       r.glast = a.ws_gam[item * C + C - 1];
     };
-    auto step = [&](int c, SRegs &r) __attribute__((always_inline)) {
+    auto step = [&](int c, SRegs &r, SRegs &free_set) __attribute__((always_inline)) {
+      // the chunk kDepth - 1 ahead into the set chunk c - 1 used, in the
+      // half of the step where this wave waits anyway
+      load(min(c + kDepth - 1, nchunks - 1), free_set);
       __syncthreads();  // U' ready; every read of sb done
       bf16x8 bu[C / 16];
       load_upt(bu);
@@ -571,7 +587,6 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
       for (int e = 0; e < 16; ++e) st[e] *= r.glast;
 #pragma unroll
       for (int ks = 0; ks < C / 16; ++ks) st = mfma(r.kd[ks], bu[ks], st);
-      load(min(c + kDepth, nchunks - 1), r);
       store_state();
       __syncthreads();  // the new state ready
     };
@@ -579,10 +594,11 @@ __global__ __launch_bounds__(kScanWaves * 64, 1) void gdn_scan(const GdnArgs a) 
     SRegs r[kDepth];
     if (nchunks > 0) {
 #pragma unroll
-      for (int d = 0; d < kDepth; ++d) load(min(d, nchunks - 1), r[d]);
+      for (int d = 0; d < kDepth - 1; ++d) load(min(d, nchunks - 1), r[d]);
     }
     __syncthreads();  // initial state in sb
     run_chunks(nchunks, r, step);
+    drain_loads();
     if (a.s_final != nullptr) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
