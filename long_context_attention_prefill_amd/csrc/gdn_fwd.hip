@@ -206,18 +206,30 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
         const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(kl + (32 * bi + l32) * RB + 16 * ks + 8 * g);
         const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(ql + (32 * bi + l32) * RB + 16 * ks + 8 * g);
         const bf16x8 bk = *reinterpret_cast<const bf16x8 *>(kl + (32 * bj + l32) * RB + 16 * ks + 8 * g);
-        kk = mfma(ak, bk, kk);
-        qk = mfma(aq, bk, qk);
+        // transposed products: the lane's column is row i of the block
+        kk = mfma(bk, ak, kk);
+        qk = mfma(bk, aq, qk);
       }
     }
-    const int j = 32 * bj + l32;
-    const float gj = gam_s[j];
+    // entry 4 jj + e of lane (l32, g): i = 32 bi + l32, j = 32 bj + 8 jj + 4 g + e,
+    // so each lane writes rows of four consecutive j (16-byte A rows in LDS,
+    // 8-byte pieces of P that a wave's store lays down as 512 contiguous bytes)
+    const int i = 32 * bi + l32;
+    const float gi = gam_s[i], bti = beta_s[i];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int i = 32 * bi + acc_row(e, g);
-      const float dec = i >= j ? exp2_fast(gam_s[i] - gj) : 0.0f;  // Gam_i / Gam_j <= 1 for i >= j
-      af[i * RF4 + j] = i > j ? beta_s[i] * dec * kk[e] : 0.0f;
-      p_out[frag_index(i, j, C / 16)] = (__bf16)(a.scale * dec * qk[e]);
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j0 = 32 * bj + 8 * jj + 4 * g;
+      f32x4 arow;
+      bf16x4 prow;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + e;
+        const float dec = i >= j ? exp2_fast(gi - gam_s[j]) : 0.0f;  // Gam_i / Gam_j <= 1 for i >= j
+        arow[e] = i > j ? bti * dec * kk[4 * jj + e] : 0.0f;
+        prow[e] = (__bf16)(a.scale * dec * qk[4 * jj + e]);
+      }
+      *reinterpret_cast<f32x4 *>(af + i * RF4 + j0) = arow;
+      *reinterpret_cast<bf16x4 *>(p_out + frag_index(i, j0, C / 16)) = prow;
     }
   }
   __syncthreads();  // Q is no longer read: its region takes T
@@ -292,18 +304,22 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
     *reinterpret_cast<bf16x4 *>(tbk + r * RT + 4 * cq) = xk;
     *reinterpret_cast<bf16x4 *>(tbv + r * RT + 4 * cq) = xv;
   }
-  // K^T diag(Gam_last / Gam) to the workspace: eight tokens of one key dim per task
+  // K^T diag(Gam_last / Gam) to the workspace, one 16-byte piece of its
+  // operand order per task, consecutive tasks on consecutive pieces
+  // (frag_index): key dim 32 (task >> 8) + (task & 31), tokens
+  // 16 ((task >> 6) & 3) + 8 ((task >> 5) & 1) .. +7
   for (int task = tid; task < DK * (C / 8); task += 256) {
-    const int k = task >> 3, m0 = 8 * (task & 7);
+    const int k = 32 * (task >> 8) + (task & 31), m0 = 16 * ((task >> 6) & 3) + 8 * ((task >> 5) & 1);
     bf16x8 x;
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = (__bf16)(fd_s[m0 + e] * (float)kl[(m0 + e) * RB + k]);
-    *reinterpret_cast<bf16x8 *>(kd_out + frag_index(k, m0, C / 16)) = x;
+    *reinterpret_cast<bf16x8 *>(kd_out + 8 * task) = x;
   }
   __syncthreads();
 
   // W = (T diag(beta Gam)) K, U = (T diag(beta)) V: wave w -> columns
-  // 32w .. 32w+31 of both, all 64 rows; K and V are read down their columns.
+  // 32w .. 32w+31 of both, all 64 rows; K and V are read down their columns
+  // (W computed transposed, so its rows leave as 8-byte pieces).
   {
     f32x16 wacc[2] = {(f32x16)(0.0f), (f32x16)(0.0f)};
     f32x16 uacc[2] = {(f32x16)(0.0f), (f32x16)(0.0f)};
@@ -318,14 +334,21 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
       }
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
-        wacc[ib] = mfma(*reinterpret_cast<const bf16x8 *>(tbk + (32 * ib + l32) * RT + 16 * ks + 8 * g), bw, wacc[ib]);
+        // W transposed: the lane's column is token 32 ib + l32
+        wacc[ib] = mfma(bw, *reinterpret_cast<const bf16x8 *>(tbk + (32 * ib + l32) * RT + 16 * ks + 8 * g), wacc[ib]);
         uacc[ib] = mfma(*reinterpret_cast<const bf16x8 *>(tbv + (32 * ib + l32) * RT + 16 * ks + 8 * g), bu, uacc[ib]);
       }
     }
+    // W: the lane holds token 32 ib + l32, key dims 32 wave + 8 jj + 4 g .. +3
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) w_out[frag_index(32 * ib + acc_row(e, g), col, DK / 16)] = (__bf16)wacc[ib][e];
+      for (int jj = 0; jj < 4; ++jj) {
+        bf16x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = (__bf16)wacc[ib][4 * jj + e];
+        *reinterpret_cast<bf16x4 *>(w_out + frag_index(32 * ib + l32, 32 * wave + 8 * jj + 4 * g, DK / 16)) = x;
+      }
     // U transposed, [v][t]: four consecutive tokens per store
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
