@@ -235,8 +235,8 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
   __syncthreads();  // Q is no longer read: its region takes T
 
   // T = (I + A)^-1, A strictly lower.  Diagonal 16 x 16 blocks: wave w
-  // inverts block w, lane c < 16 computing column c row by row; the rest of
-  // the lanes clear T above the block diagonal.
+  // inverts block w, lane c < 16 computing column c row by row.  T above the
+  // block diagonal is never stored: the bf16 copies below write its zeros.
   if (lane < 16) {
     const int base = 16 * wave, cc = lane;
     float col[16];
@@ -252,12 +252,6 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) tf[(base + i) * RF4 + base + cc] = col[i];
-  } else {
-    // rows 16 wave .. +15, columns of the blocks right of the diagonal
-    for (int idx = lane - 16; idx < 16 * (48 - 16 * wave); idx += 48) {
-      const int r = idx / (48 - 16 * wave), cc = 16 * (wave + 1) + idx % (48 - 16 * wave);
-      tf[(16 * wave + r) * RF4 + cc] = 0.0f;
-    }
   }
   __syncthreads();
   // Y_i = T_ii A[block i][columns < 16 i] for i = 1..3 (16 x 16i each), four
@@ -277,23 +271,27 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
   }
   __syncthreads();
   // Off-diagonal blocks by distance d: T_ij = -sum_{k in blocks j..i-1} Y_i[r][k] T[k][block j].
+#pragma unroll
   for (int d = 1; d < 4; ++d) {
     for (int task = tid; task < (4 - d) * 64; task += 256) {
       const int bj = task >> 6, bi = bj + d;
       const int r = (task >> 2) & 15, cq = task & 3;
-      const float *yrow = yf + 16 * 8 * bi * (bi - 1) + r * (16 * bi);
+      const float *yrow = yf + 16 * 8 * bi * (bi - 1) + r * (16 * bi) + 16 * bj;
+      const float *tcol = tf + 16 * bj * RF4 + 16 * bj + 4 * cq;
       f32x4 acc = (f32x4)(0.0f);
-      for (int k = 16 * bj; k < 16 * bi; ++k)
-        acc += yrow[k] * *reinterpret_cast<const f32x4 *>(tf + k * RF4 + 16 * bj + 4 * cq);
+#pragma unroll
+      for (int k = 0; k < 16 * d; ++k)
+        acc += yrow[k] * *reinterpret_cast<const f32x4 *>(tcol + k * RF4);
       *reinterpret_cast<f32x4 *>(tf + (16 * bi + r) * RF4 + 16 * bj + 4 * cq) = -acc;
     }
     __syncthreads();
   }
 
-  // bf16 T diag(beta Gam) and T diag(beta) (A and Y are no longer needed)
+  // bf16 T diag(beta Gam) and T diag(beta) (A and Y are no longer needed);
+  // T is zero right of the block diagonal
   for (int idx = tid; idx < C * C / 4; idx += 256) {
     const int r = idx >> 4, cq = idx & 15;
-    const f32x4 t = *reinterpret_cast<const f32x4 *>(tf + r * RF4 + 4 * cq);
+    const f32x4 t = cq < 4 * ((r >> 4) + 1) ? *reinterpret_cast<const f32x4 *>(tf + r * RF4 + 4 * cq) : (f32x4)(0.0f);
     bf16x4 xk, xv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
