@@ -148,30 +148,48 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
   __bf16 *q_out = reinterpret_cast<__bf16 *>(a.ws_q) + (size_t)item * C * DK;
   float *gam_out = a.ws_gam + (size_t)item * C;
 
-  // K, Q, V rows of the chunk (rows past its end are zero), gates, betas
+  // K, Q, V rows of the chunk (rows past its end are zero), gates, betas.
+  // Every load is issued before any is used (rows past the end load the
+  // last row and are replaced by zeros), so the item pays one memory
+  // latency here, not one per row group.
   const bf16x8 zero8 = (bf16x8)((__bf16)0.0f);
-  for (int idx = tid; idx < C * (DK / 8); idx += 256) {
+  constexpr int kRowLoads = C * (DK / 8) / 256;  // 16-byte pieces per thread and matrix
+  bf16x8 kv[kRowLoads], qv[kRowLoads], vv[kRowLoads];
+#pragma unroll
+  for (int it = 0; it < kRowLoads; ++it) {
+    const int idx = tid + 256 * it;
     const int r = idx >> 4, cc = idx & 15;
-    bf16x8 kv = zero8, qv = zero8, vv = zero8;
-    if (r < n) {
-      const size_t row = (size_t)(t0 + r) * a.h + h;
-      kv = *reinterpret_cast<const bf16x8 *>(K + row * DK + cc * 8);
-      qv = *reinterpret_cast<const bf16x8 *>(Q + row * DK + cc * 8);
-      vv = *reinterpret_cast<const bf16x8 *>(V + row * DV + cc * 8);
+    const size_t row = (size_t)(t0 + min(r, n - 1)) * a.h + h;
+    kv[it] = *reinterpret_cast<const bf16x8 *>(K + row * DK + cc * 8);
+    qv[it] = *reinterpret_cast<const bf16x8 *>(Q + row * DK + cc * 8);
+    vv[it] = *reinterpret_cast<const bf16x8 *>(V + row * DV + cc * 8);
+  }
+  float gx = 0.0f, gb = 0.0f;
+  if (wave == 0) {
+    const size_t th = (size_t)(t0 + min(lane, n - 1)) * a.h + h;
+    gx = a.g[th];
+    gb = a.beta[th];
+  }
+  // (stored unconditionally, then overwritten past the end: a select here
+  // lets the compiler move loads into a branch and wait inside it)
+#pragma unroll
+  for (int it = 0; it < kRowLoads; ++it) {
+    const int idx = tid + 256 * it;
+    const int r = idx >> 4, cc = idx & 15;
+    *reinterpret_cast<bf16x8 *>(kl + r * RB + cc * 8) = kv[it];
+    *reinterpret_cast<bf16x8 *>(ql + r * RB + cc * 8) = qv[it];
+    *reinterpret_cast<bf16x8 *>(vl + r * RB + cc * 8) = vv[it];
+    if (r >= n) {
+      *reinterpret_cast<bf16x8 *>(kl + r * RB + cc * 8) = zero8;
+      *reinterpret_cast<bf16x8 *>(ql + r * RB + cc * 8) = zero8;
+      *reinterpret_cast<bf16x8 *>(vl + r * RB + cc * 8) = zero8;
     }
-    *reinterpret_cast<bf16x8 *>(kl + r * RB + cc * 8) = kv;
-    *reinterpret_cast<bf16x8 *>(ql + r * RB + cc * 8) = qv;
-    *reinterpret_cast<bf16x8 *>(vl + r * RB + cc * 8) = vv;
   }
   if (wave == 0) {
     // inclusive scan of the log-gates over the chunk (padding adds 0), kept
     // in log2 units so every decay below is one exp2
-    float x = 0.0f, bt = 0.0f;
-    if (lane < n) {
-      const size_t th = (size_t)(t0 + lane) * a.h + h;
-      x = a.g[th] * kLog2e;
-      bt = a.beta[th];
-    }
+    float x = lane < n ? gx * kLog2e : 0.0f;
+    const float bt = lane < n ? gb : 0.0f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_up(x, off);
