@@ -272,35 +272,37 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
     for (int i = 0; i < 16; ++i) tf[(base + i) * RF4 + base + cc] = col[i];
   }
   __syncthreads();
-  // Y_i = T_ii A[block i][columns < 16 i] for i = 1..3 (16 x 16i each), four
-  // columns per task.  Y_i starts at yf + 16 * 8 * i * (i - 1).
-  for (int task = tid; task < 16 * (4 + 8 + 12); task += 256) {
-    const int i = task < 64 ? 1 : (task < 192 ? 2 : 3);
-    const int rel = task - (i == 1 ? 0 : (i == 2 ? 64 : 192));
-    const int r = rel / (4 * i), cq = rel % (4 * i);
+  // The rest of T by blocks, on fp32 MFMA (16 x 16 x 4: lane l supplies
+  // A[l % 16][l / 16] and B[l / 16][l % 16] of a k step and holds
+  // D[4 (l / 16) + e][l % 16]).  First Y_i = T_ii A[block i][columns < 16 i]
+  // for i = 1..3 (16 x 16i each, row stride 16i, at yf + 128 i (i - 1)):
+  // six 16 x 16 blocks (i, c), wave w taking blocks w and w + 4.
+  const int rr = lane & 15, kq = lane >> 4;
+  for (int b6 = wave; b6 < 6; b6 += 4) {
+    const int i = b6 < 1 ? 1 : (b6 < 3 ? 2 : 3), c = b6 - i * (i - 1) / 2;
     f32x4 acc = (f32x4)(0.0f);
-    const float *trow = tf + (16 * i + r) * RF4 + 16 * i;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const float t = trow[m];  // T_ii is lower triangular: zero past r
-      acc += t * *reinterpret_cast<const f32x4 *>(af + (16 * i + m) * RF4 + 4 * cq);
-    }
-    *reinterpret_cast<f32x4 *>(yf + 16 * 8 * i * (i - 1) + r * (16 * i) + 4 * cq) = acc;
+    for (int k0 = 0; k0 < 16; k0 += 4)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tf[(16 * i + rr) * RF4 + 16 * i + k0 + kq],
+                                                 af[(16 * i + k0 + kq) * RF4 + 16 * c + rr], acc, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) yf[128 * i * (i - 1) + (4 * kq + e) * (16 * i) + 16 * c + rr] = acc[e];
   }
   __syncthreads();
-  // Off-diagonal blocks by distance d: T_ij = -sum_{k in blocks j..i-1} Y_i[r][k] T[k][block j].
+  // Off-diagonal blocks by distance d: T_ij = -Y_i[:, 16j .. 16i) T[16j .. 16i, block j];
+  // wave w < 4 - d takes block (j = w, i = w + d), K = 16 d.
 #pragma unroll
   for (int d = 1; d < 4; ++d) {
-    for (int task = tid; task < (4 - d) * 64; task += 256) {
-      const int bj = task >> 6, bi = bj + d;
-      const int r = (task >> 2) & 15, cq = task & 3;
-      const float *yrow = yf + 16 * 8 * bi * (bi - 1) + r * (16 * bi) + 16 * bj;
-      const float *tcol = tf + 16 * bj * RF4 + 16 * bj + 4 * cq;
+    if (wave < 4 - d) {
+      const int bj = wave, bi = bj + d;
+      const float *yrow = yf + 128 * bi * (bi - 1) + rr * (16 * bi) + 16 * bj;
       f32x4 acc = (f32x4)(0.0f);
 #pragma unroll
-      for (int k = 0; k < 16 * d; ++k)
-        acc += yrow[k] * *reinterpret_cast<const f32x4 *>(tcol + k * RF4);
-      *reinterpret_cast<f32x4 *>(tf + (16 * bi + r) * RF4 + 16 * bj + 4 * cq) = -acc;
+      for (int k0 = 0; k0 < 16 * d; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(yrow[k0 + kq], tf[(16 * bj + k0 + kq) * RF4 + 16 * bj + rr], acc,
+                                                   0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tf[(16 * bi + 4 * kq + e) * RF4 + 16 * bj + rr] = -acc[e];
     }
     __syncthreads();
   }
