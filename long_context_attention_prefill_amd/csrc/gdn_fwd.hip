@@ -20,17 +20,18 @@
 //             chunk's K, Q, V, g, beta; cumulative gates by a wave scan;
 //             K K^T and Q K^T on MFMA; A and the masked, gated scores P;
 //             T by blocked forward substitution (16 x 16 diagonal blocks by
-//             rows, off-diagonal blocks by distance from the diagonal, fp32);
-//             W and U on MFMA; stores W, U, P, K^T diag(Gam_last / Gam) and
-//             Gam in the workspace.
+//             rows, the off-diagonal blocks by distance from the diagonal on
+//             fp32 MFMA); W and U on MFMA; stores W, U, P,
+//             K^T diag(Gam_last / Gam), Gam and a copy of Q in the
+//             workspace, in the order the scan reads them as MFMA operands.
 //   gdn_scan  (one workgroup per sequence, head and 32 state rows): carries
 //             its 32 x 128 slice of S in fp32 MFMA accumulators through the
 //             sequence's chunks in order; per chunk U' = U - W S^T and
 //             Q S^T (MFMA), O = diag(scale Gam) Q S^T + P U' (MFMA), then
-//             S <- Gam_last S + Kd U' (MFMA).  Workspace rows of the chunk
-//             after next load into registers while the current one computes;
-//             the four slices of a (sequence, head) run on one XCD.  Eight
-//             waves split the chunk step by role (see gdn_scan).
+//             S <- Gam_last S + Kd U' (MFMA).  Each wave loads its own
+//             operands of a chunk straight into registers a few chunks
+//             ahead; the four slices of a (sequence, head) run on one XCD.
+//             Eight waves split the chunk step by role (see gdn_scan).
 //
 // MFMA operands are bf16 (the state is rounded to bf16 for each product and
 // kept in fp32 between chunks); accumulation is fp32.
@@ -54,7 +55,6 @@ constexpr int DK = kDk;
 constexpr int DV = kDv;
 constexpr int RB = DK + 8;  // bf16 row stride of [*][128] LDS tiles (272 bytes: 17 16-byte slots)
 constexpr int RT = C + 8;   // bf16 row stride of [*][64] LDS tiles (144 bytes: 9 slots)
-constexpr int RU = kSliceRows + 8;  // bf16 row stride of a [*][32] staging tile
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
