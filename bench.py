@@ -391,6 +391,12 @@ def read_counters():
         return None
 
 
+def ordinal_suffix(n):
+    if n % 100 in (11, 12, 13):
+        return "th"
+    return {1: "st", 2: "nd", 3: "rd"}.get(n % 10, "th")
+
+
 def cpu_baseline(w, host_inputs, target_s=12.0):
     """The fp64 oracle, as it stands, on a bounded sample of the workload's
     rows (every head of strided rows), scaled to tokens/s by the share of
@@ -425,7 +431,7 @@ def cpu_baseline(w, host_inputs, target_s=12.0):
         "cores": threads,
         "kind": "oracle",
         "sample": (f"fp64 C oracle (OpenMP, {threads} threads) on {nrows} rows x {hq} heads "
-                   f"(every {stride}th query row), {sp / full_pairs:.4f} of the workload's "
+                   f"(every {stride}{ordinal_suffix(stride)} query row), {sp / full_pairs:.4f} of the workload's "
                    f"query-key pairs in {dt:.2f} s; scaled to the full workload: "
                    f"{est_full_s:.1f} s"),
     }
