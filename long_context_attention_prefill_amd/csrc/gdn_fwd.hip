@@ -114,7 +114,8 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kPrepLds];
-  __shared__ float gam_s[C], beta_s[C], big_s[C], fd_s[C];
+  __shared__ __attribute__((aligned(16))) float gam_s[C];
+  __shared__ float beta_s[C], big_s[C], fd_s[C];
   __bf16 *kl = reinterpret_cast<__bf16 *>(lds + kR0);
   __bf16 *vl = reinterpret_cast<__bf16 *>(lds + kR1);
   __bf16 *ql = reinterpret_cast<__bf16 *>(lds + kR2);
@@ -237,14 +238,17 @@ __global__ __launch_bounds__(256, 2) void gdn_prep(const GdnArgs a) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int j0 = 32 * bj + 8 * jj + 4 * g;
-      f32x4 arow;
-      bf16x4 prow;
+      f32x4 arow = (f32x4)(0.0f);
+      bf16x4 prow = (bf16x4)((__bf16)0.0f);
+      if (bi >= bj) {  // the block above the diagonal is zero
+        const f32x4 gj = *reinterpret_cast<const f32x4 *>(&gam_s[j0]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + e;
-        const float dec = i >= j ? exp2_fast(gi - gam_s[j]) : 0.0f;  // Gam_i / Gam_j <= 1 for i >= j
-        arow[e] = i > j ? bti * dec * kk[4 * jj + e] : 0.0f;
-        prow[e] = (__bf16)(a.scale * dec * qk[4 * jj + e]);
+        for (int e = 0; e < 4; ++e) {
+          const int j = j0 + e;
+          const float dec = i >= j ? exp2_fast(gi - gj[e]) : 0.0f;  // Gam_i / Gam_j <= 1 for i >= j
+          arow[e] = i > j ? bti * dec * kk[4 * jj + e] : 0.0f;
+          prow[e] = (__bf16)(a.scale * dec * qk[4 * jj + e]);
+        }
       }
       *reinterpret_cast<f32x4 *>(af + i * RF4 + j0) = arow;
       *reinterpret_cast<bf16x4 *>(p_out + frag_index(i, j0, C / 16)) = prow;
