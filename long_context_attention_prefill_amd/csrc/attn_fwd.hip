@@ -61,7 +61,7 @@ struct Item {
 // (s % 8) * (hq / 8) + s / 8: consecutive workgroups land on different XCDs
 // round-robin, so each XCD keeps to a contiguous block of query heads, i.e.
 // to few key/value heads, and their K/V stays in that XCD's L2.
-__device__ Item decode_item(const LaunchArgs &a, int r) {
+__device__ __forceinline__ Item decode_item(const LaunchArgs &a, int r) {
   Item it{0, 0, 0};
   int slot = 0;
   if (a.mask_kind == kCausal) {
@@ -90,6 +90,7 @@ __device__ Item decode_item(const LaunchArgs &a, int r) {
   return it;
 }
 
+// Visible keys [lo, hi) of the query at position i of a sequence of n keys.
 __device__ __forceinline__ void row_range(int mask, int W, int i, int n, int &lo, int &hi) {
   if (mask == kCausal) {
     lo = 0;
@@ -107,9 +108,15 @@ __device__ __forceinline__ void row_range(int mask, int W, int i, int n, int &lo
 // ---------------------------------------------------------------------------
 // bf16 / MFMA family, head_dim 64, 72 and 128.  K and V reach LDS by direct
 // buffer->LDS loads: no staging registers, and rows past the key range read
-// as zeros (buffer range check).  Both tiles use the padded, key-permuted
-// layout of attn_device.h, whose K row reads and V transposing reads are
-// free of bank conflicts.
+// as zeros (buffer range check).  Inside each 16-key MFMA step keys are
+// taken in the permuted order of attn_device.h.  head_dim 64 and 72 use its
+// padded layout (one 16-byte pad slot per key row); head_dim 128 stores key
+// rows unpadded, 256 bytes each, with chunk c of key k at slot c ^ (k mod 16):
+// 16 keys read by 16 lanes (K, 16-byte reads) start at 16 distinct slots,
+// and the 4 keys x 64 bytes of a V transposing read fill 4 distinct quarters
+// of the 256-byte bank window, so both are free of bank conflicts, while
+// every 64-lane load carries 1 KB of key data (the padded layout spent 4 of
+// its 20 loads per head-dim-128 tile on padding and out-of-range spill).
 // ---------------------------------------------------------------------------
 
 // Each wave owns R consecutive 32-row query sub-blocks (the workgroup covers
@@ -133,7 +140,11 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
   constexpr int CH = L::CH;
   constexpr int KST = L::KST;         // MFMA k steps of S^T (the last one zero-padded when D = 72)
   constexpr int DB = (D + 31) / 32;  // 32-row blocks of O^T (rows past D are computed and dropped)
-  constexpr int KBUF = BN * L::ROWB;  // bytes per K (or V) tile
+  // head_dim 128: unpadded 256-byte key rows whose 16-byte chunk c sits at
+  // slot c ^ (key mod 16) (the XOR layout); 64 and 72: the padded layout
+  constexpr bool XOR = D == 128;
+  constexpr int ROWB = XOR ? D * 2 : L::ROWB;  // bytes per key row in LDS
+  constexpr int KBUF = BN * ROWB;  // bytes per K (or V) tile
   // A tile is NLOADS wave-wide direct loads (64 lanes x 16 bytes); each wave
   // issues NL of them, and a wave whose last load falls past the tile sends
   // it, all lanes out of range, into a 1 KB spill slot after the tile, so
@@ -219,15 +230,22 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
                                                    : (bf16x8)((__bf16)0.0f);
   }
 
-  // Direct loads: wave-wide load j fills LDS slots 64j .. 64j+63 of a tile;
-  // slot p is row p / SLOTS, chunk p % SLOTS (chunks >= CH are padding).
+  // Direct loads: wave-wide load j fills LDS slots 64j .. 64j+63 of a tile.
+  // Padded layout: slot p is row p / SLOTS, chunk p % SLOTS (chunks >= CH are
+  // padding).  XOR layout: load j fills keys 4j .. 4j+3, lane l writing key
+  // 4j + (l >> 4), slot l & 15, which holds chunk (l & 15) ^ (key & 15).
   const int rowbytes = a.kv_stride * 2;  // bytes between consecutive tokens of one head
   uint32_t ld_off[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const int p = (wave + NW * i) * 64 + lane;
-    const int rr = p / L::SLOTS, cs = p % L::SLOTS;
-    ld_off[i] = cs < CH ? (uint32_t)(rr * rowbytes + cs * 16) : kOutOfRange;
+    if constexpr (XOR) {
+      const int key = 4 * (wave + NW * i) + (lane >> 4);
+      ld_off[i] = (uint32_t)(key * rowbytes + ((lane & 15) ^ (key & 15)) * 16);
+    } else {
+      const int p = (wave + NW * i) * 64 + lane;
+      const int rr = p / L::SLOTS, cs = p % L::SLOTS;
+      ld_off[i] = cs < CH ? (uint32_t)(rr * rowbytes + cs * 16) : kOutOfRange;
+    }
   }
   const char *kseq = reinterpret_cast<const char *>(a.k) + ((size_t)s0k * a.kv_stride + (size_t)hk * D) * 2;
   const char *vseq = reinterpret_cast<const char *>(a.v) + ((size_t)s0k * a.kv_stride + (size_t)hk * D) * 2;
@@ -255,8 +273,47 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
   //   second half of a k step, +16 per k step) and columns
   //   32db + 16*(lane>>4 & 1) + 4q .. +3; the transpose hands lane j of the
   //   group column j of those four keys, in the order P holds them.
-  const int kread = key_of_row(l32) * L::ROWB + 16 * g;
-  const int vread = (g + 4 * ((lane & 15) >> 2)) * L::ROWB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  const int kread = key_of_row(l32) * ROWB + 16 * g;
+  const int vread = (g + 4 * ((lane & 15) >> 2)) * ROWB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  // XOR layout: chunk 2kk + g of key k sits at slot (2kk + g) ^ (k & 15), i.e.
+  // at kaddr ^ 32 kk; the V chunk a lane reads for block db (and for the
+  // second half of a k step, two keys on) sits at its db = 0 slot XOR 4 db
+  // (XOR 2), so each fragment read has its own per-lane address.
+  uint32_t kaddr[XOR ? KST : 1], vaddr[XOR ? DB : 1][2];
+  if constexpr (XOR) {
+    const int key = key_of_row(l32);
+    const int k0 = key * ROWB + ((g ^ (key & 1)) | (key & 14)) * 16;
+#pragma unroll
+    for (int kk = 0; kk < KST; ++kk) kaddr[kk] = (uint32_t)(k0 ^ (32 * kk));
+    const int r4 = (lane & 15) >> 2, q4 = lane & 3, hb = (lane >> 4) & 1;
+    const int key0 = g + 4 * r4;
+    const int v0 = key0 * ROWB + ((2 * hb + (q4 >> 1)) ^ key0) * 16 + 8 * (q4 & 1);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) vaddr[db][hi] = (uint32_t)((v0 ^ (64 * db) ^ (32 * hi)) + 2 * ROWB * hi);
+  }
+  // K fragment (A operand of S^T, k step kk of 32-key block nb) and V^T
+  // fragment (A operand of O^T, k step ks, block db) of the tile at buf.
+  auto kfrag = [&](const char *buf, int nb, int kk) __attribute__((always_inline)) -> bf16x8 {
+    if constexpr (XOR)
+      return *reinterpret_cast<const bf16x8 *>(buf + kaddr[kk] + nb * 32 * ROWB);
+    else
+      return *reinterpret_cast<const bf16x8 *>(buf + kread + nb * 32 * ROWB + kk * 32);
+  };
+  auto vfrag = [&](const char *buf, int ks, int db) __attribute__((always_inline)) -> bf16x8 {
+    const char *lo_p, *hi_p;
+    if constexpr (XOR) {
+      lo_p = buf + vaddr[db][0] + ks * 16 * ROWB;
+      hi_p = buf + vaddr[db][1] + ks * 16 * ROWB;
+    } else {
+      lo_p = buf + vread + ks * 16 * ROWB + db * 64;
+      hi_p = lo_p + 2 * ROWB;
+    }
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)lo_p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)hi_p);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
   f32x16 o[R][DB];
   float l_run[R];  // this lane's share of each row sum
@@ -292,14 +349,14 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
   // S^T = K Q^T for the 64 keys held in K buffer KB, every sub-block; each K
   // fragment feeds the R sub-blocks' MFMAs in a row.
   auto qk = [&](auto kbuf_tag, f32x16 (&sc)[R][2]) {
-    const char *kb = k_buf(kbuf_tag) + kread;
+    const char *kb = k_buf(kbuf_tag);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
       for (int r = 0; r < R; ++r) sc[r][nb] = (f32x16)(0.0f);
 #pragma unroll
       for (int kk = 0; kk < KST; ++kk) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + nb * 32 * L::ROWB + kk * 32);
+        const bf16x8 kf = kfrag(kb, nb, kk);
 #pragma unroll
         for (int r = 0; r < R; ++r)
           sc[r][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[r][kk], sc[r][nb], 0, 0, 0);
@@ -392,16 +449,12 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
   // O += P V with V from V buffer VB; each V fragment feeds the R
   // sub-blocks' MFMAs in a row.
   auto pv = [&](auto vbuf_tag, const bf16x8 (&pf)[R][BN / 16]) {
-    const char *vb = v_buf(vbuf_tag) + vread;
+    const char *vb = v_buf(vbuf_tag);
 #pragma unroll
     for (int ks = 0; ks < BN / 16; ++ks)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const char *vp = vb + ks * 16 * L::ROWB + db * 64;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp + 2 * L::ROWB));
-        const bf16x8 vf = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 vf = vfrag(vb, ks, db);
 #pragma unroll
         for (int r = 0; r < R; ++r)
           o[r][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[r][ks], o[r][db], 0, 0, 0);
@@ -454,14 +507,14 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
     if (wave_sees(t)) {
       f32x16 sc[R][2];
       {
-        const char *kb = k_rt(buf) + kread;
+        const char *kb = k_rt(buf);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
           for (int r = 0; r < R; ++r) sc[r][nb] = (f32x16)(0.0f);
 #pragma unroll
           for (int kk = 0; kk < KST; ++kk) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kb + nb * 32 * L::ROWB + kk * 32);
+            const bf16x8 kf = kfrag(kb, nb, kk);
 #pragma unroll
             for (int r = 0; r < R; ++r)
               sc[r][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[r][kk], sc[r][nb], 0, 0, 0);
@@ -478,17 +531,12 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
       bf16x8 pf[R][BN / 16];
       softmax(sc, pf);
       {
-        const char *vb = v_rt(buf) + vread;
+        const char *vb = v_rt(buf);
 #pragma unroll
         for (int ks = 0; ks < BN / 16; ++ks)
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const char *vp = vb + ks * 16 * L::ROWB + db * 64;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp));
-            const i16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vp + 2 * L::ROWB));
-            const bf16x8 vf = __builtin_bit_cast(
-                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            const bf16x8 vf = vfrag(vb, ks, db);
 #pragma unroll
             for (int r = 0; r < R; ++r)
               o[r][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[r][ks], o[r][db], 0, 0, 0);
