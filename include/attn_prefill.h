@@ -209,6 +209,29 @@ int attn_decode_workspace_size(const int32_t *cu_seqlens_k, int32_t n_seqs,
                                int32_t mask_kind, int32_t window,
                                uint64_t *bytes);
 
+/*
+ * attn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and arguments as attn_decode, with the
+ * workspace taken from a static device array of the library
+ * (ATTN_DECODE_SCRATCH_BYTES, 16 MiB, one per GPU, held until the process
+ * ends) instead of a caller buffer.  The array of the device the stream
+ * belongs to (the current device for a NULL stream) is looked up on the first
+ * call on that device; the call allocates nothing.  Every call on one GPU
+ * shares that GPU's array, which keeps the last call's contents: calls that
+ * overlap on one GPU (different streams or threads without ordering) race,
+ * so callers order them.
+ *
+ * Returns the codes of attn_decode, plus ATTN_EUNSUPPORTED when the shape
+ * needs more workspace than the array holds (attn_decode_workspace_size
+ * reports that need) and ATTN_ELAUNCH when the array cannot be located.
+ */
+#define ATTN_DECODE_SCRATCH_BYTES 16777216 /* 16 MiB */
+int attn_decode_noalloc(const void *q, const void *k, const void *v, void *out, float *lse,
+                        const int32_t *cu_seqlens_k, int32_t n_seqs, int32_t n_q_heads,
+                        int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                        int32_t mask_kind, int32_t window, float scale, void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *attn_strerror(int status);
 

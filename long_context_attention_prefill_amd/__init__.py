@@ -10,6 +10,10 @@ functions carry the C entry points' names:
   sequence (chunked prefill, decode), optionally with the log-sum-exp
 * ``attn_decode(q, k, v, cu_seqlens_k, mask="causal", scale=None, out=None,
   lse=False, workspace=None)`` -- one query per sequence over its cache
+* ``attn_decode_noalloc(q, k, v, cu_seqlens_k, mask="causal", scale=None,
+  out=None, lse=False)`` -- the same with the library's static device
+  workspace (for callers that cannot allocate; calls on one GPU must not
+  overlap)
 * ``attn_prefill_check(...)``, ``attn_prefill_kv_check(...)``,
   ``attn_decode_workspace_size(...)``, ``attn_strerror(status)``,
   ``attn_version()``
@@ -34,17 +38,19 @@ import math
 import os
 
 __all__ = ["attn_prefill", "attn_prefill_check", "attn_prefill_kv", "attn_prefill_kv_check",
-           "attn_decode", "attn_decode_workspace_size", "attn_strerror", "attn_version",
+           "attn_decode", "attn_decode_noalloc", "attn_decode_workspace_size", "attn_strerror",
+           "attn_version",
            "gdn_prefill", "gdn_prefill_workspace_size", "proj_dequantize_int8", "proj_linear",
            "vision_attention_block", "vision_attention_block_workspace_size",
            "AttnError", "library_path", "load_library", "ATTN_OK", "ATTN_EINVAL",
            "ATTN_EUNSUPPORTED", "ATTN_ELAUNCH", "ATTN_BF16", "ATTN_F32", "ATTN_CAUSAL",
-           "ATTN_FULL", "ATTN_WINDOW"]
+           "ATTN_FULL", "ATTN_WINDOW", "ATTN_DECODE_SCRATCH_BYTES"]
 
 # values of include/attn_prefill.h
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ELAUNCH = 0, -1, -2, -3
 ATTN_BF16, ATTN_F32 = 1, 2
 ATTN_CAUSAL, ATTN_FULL, ATTN_WINDOW = 0, 1, 2
+ATTN_DECODE_SCRATCH_BYTES = 16777216
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -89,6 +95,9 @@ def load_library() -> ctypes.CDLL:
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, ip, i32, i32, i32, i32, i32, i32, i32,
                                 ctypes.c_float, vp, ctypes.c_uint64, vp]
     lib.attn_decode.restype = ctypes.c_int
+    lib.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, ip, i32, i32, i32, i32, i32, i32, i32,
+                                        ctypes.c_float, vp]
+    lib.attn_decode_noalloc.restype = ctypes.c_int
     lib.attn_decode_workspace_size.argtypes = [ip, i32, i32, i32, i32, i32, i32, i32,
                                                ctypes.POINTER(ctypes.c_uint64)]
     lib.attn_decode_workspace_size.restype = ctypes.c_int
@@ -331,6 +340,34 @@ def attn_decode(q, k, v, cu_seqlens_k, mask="causal", scale=None, out=None, lse=
                              ws_ptr, ws_bytes, ctypes.c_void_p(handle))
     if status != ATTN_OK:
         raise AttnError(status, "attn_decode")
+    return out if lse_t is None else (out, lse_t)
+
+
+def attn_decode_noalloc(q, k, v, cu_seqlens_k, mask="causal", scale=None, out=None, lse=False,
+                        stream=None):
+    """attn_decode without a workspace argument: the library's static device
+    array serves as the workspace (include/attn_prefill.h).  Pass ``out``
+    (and an ``lse`` tensor) to keep the call free of allocations."""
+    import torch
+
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q)
+    lse_t = None
+    if lse is True:
+        lse_t = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    elif lse is not False and lse is not None:
+        lse_t = lse
+    n = q.shape[0]
+    a = _args_kv(q, k, v, out, lse_t, list(range(n + 1)), cu_seqlens_k, mask, scale)
+    qp, kp, vp_, op, lp, _, cu_k, n_seqs, hq, hkv, d, dt, kind, window, sc = a
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream or 0)
+    status = lib.attn_decode_noalloc(qp, kp, vp_, op, lp, cu_k, n_seqs, hq, hkv, d, dt, kind, window,
+                                     sc, ctypes.c_void_p(handle))
+    if status != ATTN_OK:
+        raise AttnError(status, "attn_decode_noalloc")
     return out if lse_t is None else (out, lse_t)
 
 

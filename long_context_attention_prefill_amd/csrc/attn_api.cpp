@@ -14,7 +14,9 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
+
+static_assert(ATTN_DECODE_SCRATCH_BYTES == attn::kDecodeScratchBytes, "one scratch size");
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -238,6 +240,22 @@ int check_decode(const void *q, const void *k, const void *v, const void *out, c
                scale, &Tq, &Tk);
 }
 
+// Workspace bytes of a checked decode shape: the largest over its launches.
+uint64_t decode_need(const int32_t *cu_seqlens_k, int32_t n_seqs, int32_t n_q_heads,
+                     int32_t n_kv_heads, int32_t head_dim, int32_t dtype, int32_t mask_kind,
+                     int32_t window) {
+  if (n_seqs == 0 || !decode_fast(dtype, head_dim)) return 0;
+  uint64_t total = 0;
+  for (int32_t base = 0; base < n_seqs; base += attn::kMaxDecodeSeqsPerLaunch) {
+    const int32_t cnt = std::min(n_seqs - base, attn::kMaxDecodeSeqsPerLaunch);
+    std::vector<int32_t> cu(cnt + 1);
+    for (int32_t i = 0; i <= cnt; ++i) cu[i] = cu_seqlens_k[base + i] - cu_seqlens_k[base];
+    const DecodePlan p = plan_decode(cu.data(), cnt, n_q_heads, n_kv_heads, mask_kind, window);
+    total = std::max(total, decode_workspace_bytes(p, head_dim));
+  }
+  return total;
+}
+
 }  // namespace
 
 namespace attn {
@@ -310,17 +328,8 @@ int attn_decode_workspace_size(const int32_t *cu_seqlens_k, int32_t n_seqs, int3
   const int rc = check_decode_shape(cu_seqlens_k, n_seqs, n_q_heads, n_kv_heads, head_dim, dtype,
                                     mask_kind, window, 1.0f, &cu_q);
   if (rc != ATTN_OK) return rc;
-  *bytes = 0;
-  if (n_seqs == 0 || !decode_fast(dtype, head_dim)) return ATTN_OK;
-  uint64_t total = 0;
-  for (int32_t base = 0; base < n_seqs; base += attn::kMaxDecodeSeqsPerLaunch) {
-    const int32_t cnt = std::min(n_seqs - base, attn::kMaxDecodeSeqsPerLaunch);
-    std::vector<int32_t> cu(cnt + 1);
-    for (int32_t i = 0; i <= cnt; ++i) cu[i] = cu_seqlens_k[base + i] - cu_seqlens_k[base];
-    const DecodePlan p = plan_decode(cu.data(), cnt, n_q_heads, n_kv_heads, mask_kind, window);
-    total = std::max(total, decode_workspace_bytes(p, head_dim));
-  }
-  *bytes = total;
+  *bytes = decode_need(cu_seqlens_k, n_seqs, n_q_heads, n_kv_heads, head_dim, dtype, mask_kind,
+                       window);
   return ATTN_OK;
 }
 
@@ -398,6 +407,24 @@ int attn_decode(const void *q, const void *k, const void *v, void *out, float *l
   for (const attn::DecodeArgs &a : plan)
     if (attn::launch_decode_bf16(a, head_dim, stream) != 0) return ATTN_ELAUNCH;
   return ATTN_OK;
+}
+
+int attn_decode_noalloc(const void *q, const void *k, const void *v, void *out, float *lse,
+                        const int32_t *cu_seqlens_k, int32_t n_seqs, int32_t n_q_heads,
+                        int32_t n_kv_heads, int32_t head_dim, int32_t dtype, int32_t mask_kind,
+                        int32_t window, float scale, void *stream) {
+  std::vector<int32_t> cu_q;
+  const int rc = check_decode(q, k, v, out, lse, cu_seqlens_k, n_seqs, n_q_heads, n_kv_heads,
+                              head_dim, dtype, mask_kind, window, scale, &cu_q);
+  if (rc != ATTN_OK || n_seqs == 0) return rc;
+  const uint64_t need = decode_need(cu_seqlens_k, n_seqs, n_q_heads, n_kv_heads, head_dim, dtype,
+                                    mask_kind, window);
+  if (need > attn::kDecodeScratchBytes) return ATTN_EUNSUPPORTED;
+  void *scratch = nullptr;
+  if (need > 0 && attn::decode_scratch(stream, &scratch) != 0) return ATTN_ELAUNCH;
+  return attn_decode(q, k, v, out, lse, cu_seqlens_k, n_seqs, n_q_heads, n_kv_heads, head_dim,
+                     dtype, mask_kind, window, scale, scratch,
+                     need > 0 ? attn::kDecodeScratchBytes : 0, stream);
 }
 
 const char *attn_strerror(int status) {

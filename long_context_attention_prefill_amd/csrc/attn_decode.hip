@@ -6,6 +6,8 @@
 // query over its visible keys (bottom-right alignment: the query is the last
 // position of its sequence).
 #include <hip/hip_runtime.h>
+
+#include <mutex>
 #include <stdint.h>
 
 #include <type_traits>
@@ -320,6 +322,44 @@ __global__ __launch_bounds__(256) void decode_merge(const DecodeArgs a) {
 constexpr int kMergeWideFrom = 256;
 
 }  // namespace
+
+// The decode workspace of attn_decode_noalloc: one copy per device (each
+// device's code object holds its own), alive until the process ends.  Host
+// code never uses the array's name as an address: decode_scratch() looks up
+// each device's copy once, with that device current, and hands out that
+// address.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int decode_scratch(void *stream, void **ptr) {
+  int dev = 0;
+  hipError_t e = stream != nullptr ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
+                                   : hipGetDevice(&dev);
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (dev < 0 || dev >= kMaxDevices) return static_cast<int>(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return static_cast<int>(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return static_cast<int>(e);
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return static_cast<int>(e);
+    if (p == nullptr) return static_cast<int>(hipErrorInvalidSymbol);
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return 0;
+}
 
 int launch_decode_bf16(const DecodeArgs &a, int head_dim, void *stream) {
   if (a.total_items == 0) return 0;

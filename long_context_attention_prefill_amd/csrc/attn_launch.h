@@ -97,6 +97,14 @@ int launch_f32(const LaunchArgs &a, int head_dim, void *stream);
 // Decode (bf16, head_dim 64 or 128): the partial kernel, then, in split
 // mode, the merge kernel; both on `stream`.
 int launch_decode_bf16(const DecodeArgs &a, int head_dim, void *stream);
+
+// Decode workspace the library holds itself (attn_decode_noalloc): a static
+// device array of this many bytes on every GPU the library runs on.
+constexpr uint64_t kDecodeScratchBytes = 16ull << 20;
+// The device address of that array on the device `stream` belongs to (the
+// current device for the null stream), looked up once per device; 0 or a
+// hipError_t value.
+int decode_scratch(void *stream, void **ptr);
 // Query rows per workgroup of each family (the planner tiles with it).
 int rows_per_workgroup_bf16(int head_dim);
 int rows_per_workgroup_f32(int head_dim);

@@ -194,3 +194,23 @@ def test_decode_rejects_before_any_device_work(lib):
     assert call(W_, need, cu=empty) == lcap.ATTN_EINVAL  # a sequence without keys
     assert lib.attn_decode(0, 0, 0, 0, None, None, 0, 16, 2, 128, 1, 0, 0, ctypes.c_float(0.1),
                            None, 0, None) == 0
+
+
+def test_decode_noalloc_rejects_shapes_beyond_its_scratch(lib):
+    """A decode whose workspace exceeds the static scratch is refused before any
+    device work (host-only check; the fake pointers are never touched)."""
+    cu = [0]
+    for _ in range(64):
+        cu.append(cu[-1] + 100000)
+    need = lcap.attn_decode_workspace_size(cu, 64, 2, 128, lcap.ATTN_BF16, "causal")
+    assert need > lcap.ATTN_DECODE_SCRATCH_BYTES
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    # the caches span 3.3 GB each: fake addresses far enough apart not to overlap
+    kk, vv = 0x1000000000, 0x2000000000
+    st = lib.attn_decode_noalloc(Q, kk, vv, O, None, arr, 64, 64, 2, 128, 1, 0, 0,
+                                 ctypes.c_float(0.1), None)
+    assert st == lcap.ATTN_EUNSUPPORTED
+    # argument errors come first, as for attn_decode
+    st = lib.attn_decode_noalloc(None, kk, vv, O, None, arr, 64, 64, 2, 128, 1, 0, 0,
+                                 ctypes.c_float(0.1), None)
+    assert st == lcap.ATTN_EINVAL
