@@ -165,6 +165,24 @@ def _cu_array(cu_seqlens):
     return arr, len(vals) - 1
 
 
+def _stream_of(stream, device):
+    """The torch stream a call's kernels run on: ``stream`` (a torch stream or
+    a raw hipStream_t handle), else torch's current stream.  Tensors a call
+    allocates (outputs, workspaces) are allocated on this stream, so the
+    caching allocator never hands their memory to other work before the
+    call's kernels are done with it."""
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    handle = int(stream)
+    if handle == 0:
+        return torch.cuda.default_stream(device)
+    return torch.cuda.ExternalStream(handle, device=device)
+
+
 def _args(q, k, v, out, cu_seqlens, mask, scale):
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("q must be [T, Hq, d]; k and v [T, Hkv, d]")
@@ -197,13 +215,12 @@ def attn_prefill(q, k, v, cu_seqlens, mask="causal", scale=None, out=None, strea
     import torch
 
     lib = load_library()
+    st = _stream_of(stream, q.device)
     if out is None:
-        out = torch.empty_like(q)
+        with torch.cuda.stream(st):
+            out = torch.empty_like(q)
     a = _args(q, k, v, out, cu_seqlens, mask, scale)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream or 0)
-    status = lib.attn_prefill(*a, ctypes.c_void_p(handle))
+    status = lib.attn_prefill(*a, ctypes.c_void_p(st.cuda_stream))
     if status != ATTN_OK:
         raise AttnError(status)
     return out
@@ -262,18 +279,17 @@ def attn_prefill_kv(q, k, v, cu_seqlens_q, cu_seqlens_k, mask="causal", scale=No
     import torch
 
     lib = load_library()
-    if out is None:
-        out = torch.empty_like(q)
-    lse_t = None
-    if lse is True:
-        lse_t = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
-    elif lse is not False and lse is not None:
-        lse_t = lse
+    st = _stream_of(stream, q.device)
+    with torch.cuda.stream(st):
+        if out is None:
+            out = torch.empty_like(q)
+        lse_t = None
+        if lse is True:
+            lse_t = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+        elif lse is not False and lse is not None:
+            lse_t = lse
     a = _args_kv(q, k, v, out, lse_t, cu_seqlens_q, cu_seqlens_k, mask, scale)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream or 0)
-    status = lib.attn_prefill_kv(*a, ctypes.c_void_p(handle))
+    status = lib.attn_prefill_kv(*a, ctypes.c_void_p(st.cuda_stream))
     if status != ATTN_OK:
         raise AttnError(status, "attn_prefill_kv")
     return out if lse_t is None else (out, lse_t)
@@ -316,13 +332,15 @@ def attn_decode(q, k, v, cu_seqlens_k, mask="causal", scale=None, out=None, lse=
     import torch
 
     lib = load_library()
-    if out is None:
-        out = torch.empty_like(q)
-    lse_t = None
-    if lse is True:
-        lse_t = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
-    elif lse is not False and lse is not None:
-        lse_t = lse
+    st = _stream_of(stream, q.device)
+    with torch.cuda.stream(st):
+        if out is None:
+            out = torch.empty_like(q)
+        lse_t = None
+        if lse is True:
+            lse_t = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+        elif lse is not False and lse is not None:
+            lse_t = lse
     n = q.shape[0]
     cu_q = list(range(n + 1))
     a = _args_kv(q, k, v, out, lse_t, cu_q, cu_seqlens_k, mask, scale)
@@ -330,14 +348,12 @@ def attn_decode(q, k, v, cu_seqlens_k, mask="causal", scale=None, out=None, lse=
     if workspace is None:
         need = attn_decode_workspace_size(cu_seqlens_k, hq, hkv, d, dt, mask)
         if need > 0:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            with torch.cuda.stream(st):
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = None if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream or 0)
     status = lib.attn_decode(qp, kp, vp_, op, lp, cu_k, n_seqs, hq, hkv, d, dt, kind, window, sc,
-                             ws_ptr, ws_bytes, ctypes.c_void_p(handle))
+                             ws_ptr, ws_bytes, ctypes.c_void_p(st.cuda_stream))
     if status != ATTN_OK:
         raise AttnError(status, "attn_decode")
     return out if lse_t is None else (out, lse_t)
@@ -351,21 +367,20 @@ def attn_decode_noalloc(q, k, v, cu_seqlens_k, mask="causal", scale=None, out=No
     import torch
 
     lib = load_library()
-    if out is None:
-        out = torch.empty_like(q)
-    lse_t = None
-    if lse is True:
-        lse_t = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
-    elif lse is not False and lse is not None:
-        lse_t = lse
+    st = _stream_of(stream, q.device)
+    with torch.cuda.stream(st):
+        if out is None:
+            out = torch.empty_like(q)
+        lse_t = None
+        if lse is True:
+            lse_t = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+        elif lse is not False and lse is not None:
+            lse_t = lse
     n = q.shape[0]
     a = _args_kv(q, k, v, out, lse_t, list(range(n + 1)), cu_seqlens_k, mask, scale)
     qp, kp, vp_, op, lp, _, cu_k, n_seqs, hq, hkv, d, dt, kind, window, sc = a
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream or 0)
     status = lib.attn_decode_noalloc(qp, kp, vp_, op, lp, cu_k, n_seqs, hq, hkv, d, dt, kind, window,
-                                     sc, ctypes.c_void_p(handle))
+                                     sc, ctypes.c_void_p(st.cuda_stream))
     if status != ATTN_OK:
         raise AttnError(status, "attn_decode_noalloc")
     return out if lse_t is None else (out, lse_t)
@@ -413,13 +428,15 @@ def gdn_prefill(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None, ou
     cu, n = _cu_array(cu_seqlens)
     if n >= 0 and int(cu[n]) != T:
         raise ValueError("cu_seqlens[-1] must equal T")
-    if out is None:
-        out = torch.empty_like(v)
-    fin = None
-    if final_state is True:
-        fin = torch.empty((max(n, 0), H, dv, dk), dtype=torch.float32, device=q.device)
-    elif final_state is not False and final_state is not None:
-        fin = final_state
+    st = _stream_of(stream, q.device)
+    with torch.cuda.stream(st):
+        if out is None:
+            out = torch.empty_like(v)
+        fin = None
+        if final_state is True:
+            fin = torch.empty((max(n, 0), H, dv, dk), dtype=torch.float32, device=q.device)
+        elif final_state is not False and final_state is not None:
+            fin = final_state
     for name, t in (("initial_state", initial_state), ("final_state", fin)):
         if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (n, H, dv, dk)
                               or not t.is_contiguous()):
@@ -427,12 +444,11 @@ def gdn_prefill(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None, ou
     if workspace is None:
         need = gdn_prefill_workspace_size(cu_seqlens, H, dk, dv, _dtype_code(q))
         if need > 0:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            with torch.cuda.stream(st):
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = None if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream or 0)
+    handle = st.cuda_stream
     status = lib.gdn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
                              beta.data_ptr(),
                              None if initial_state is None else initial_state.data_ptr(),
@@ -446,11 +462,7 @@ def gdn_prefill(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None, ou
 
 
 def _handle(stream, device):
-    import torch
-
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream or 0))
+    return ctypes.c_void_p(_stream_of(stream, device).cuda_stream)
 
 
 def proj_dequantize_int8(q, scale, out=None, stream=None):
@@ -462,7 +474,8 @@ def proj_dequantize_int8(q, scale, out=None, stream=None):
     if scale.dtype != torch.float32 or tuple(scale.shape) != (q.shape[0],) or not scale.is_contiguous():
         raise ValueError("scale must be a contiguous float32 [N] tensor")
     if out is None:
-        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        with torch.cuda.stream(_stream_of(stream, q.device)):
+            out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     if out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 tensor of q's shape")
     status = load_library().proj_dequantize_int8(q.data_ptr(), scale.data_ptr(), out.data_ptr(),
@@ -485,7 +498,8 @@ def proj_linear(x, w, out=None, stream=None):
     T, K = (int(s) for s in x.shape)
     N = int(w.shape[0])
     if out is None:
-        out = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+        with torch.cuda.stream(_stream_of(stream, x.device)):
+            out = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
     if out.dtype != torch.bfloat16 or tuple(out.shape) != (T, N) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 [T, N] tensor")
     status = load_library().proj_linear(x.data_ptr(), w.data_ptr(), out.data_ptr(), T, N, K,
@@ -528,8 +542,10 @@ def vision_attention_block(x, w_qkv, b_qkv, w_o, b_o, cu_seqlens, n_heads, mask=
     if tuple(w_qkv.shape) != (3 * H * d, hidden) or tuple(b_qkv.shape) != (3 * H * d,) \
             or tuple(w_o.shape) != (hidden, H * d) or tuple(b_o.shape) != (hidden,):
         raise ValueError("weight shapes disagree with x and n_heads")
+    st = _stream_of(stream, x.device)
     if out is None:
-        out = torch.empty_like(x)
+        with torch.cuda.stream(st):
+            out = torch.empty_like(x)
     for name, t in (("x", x), ("w_qkv", w_qkv), ("b_qkv", b_qkv), ("w_o", w_o), ("b_o", b_o), ("out", out)):
         if t.dtype != x.dtype or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous and of x's dtype")
@@ -544,11 +560,12 @@ def vision_attention_block(x, w_qkv, b_qkv, w_o, b_o, cu_seqlens, n_heads, mask=
         raise ValueError("cu_seqlens[-1] must equal the number of packed tokens")
     if workspace is None:
         need = vision_attention_block_workspace_size(T, H, d, hidden, code)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        with torch.cuda.stream(st):
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     status = load_library().vision_attention_block(
         x.data_ptr(), w_qkv.data_ptr(), b_qkv.data_ptr(), w_o.data_ptr(), b_o.data_ptr(), out.data_ptr(),
         cu, n_seqs, H, d, hidden, code, kind, window, float(scale), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _handle(stream, x.device))
+        workspace.numel() * workspace.element_size(), ctypes.c_void_p(st.cuda_stream))
     if status != ATTN_OK:
         raise AttnError(status, "vision_attention_block")
     return out
