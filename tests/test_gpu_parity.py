@@ -100,6 +100,9 @@ def _sample_rows(cu, hq, rng, per_seq=12):
 
 @pytest.mark.parametrize("name", ["1", "2", "3", "4", "5a", "5b"])
 def test_workload_parity(orc, name):
+    """Element by element against the oracle: every element up to 2048 tokens;
+    beyond, every row of one query head per key/value head (heads 0 and 8 at
+    16/2 heads) and sampled rows (first, last, middle, random) of every head."""
     w = W.WORKLOADS[name]
     q, k, v, cu = W.make_inputs(w)
     print(f"[workload {name}] {w.name}", flush=True)
@@ -108,6 +111,14 @@ def test_workload_parity(orc, name):
         want = orc.attention(q, k, v, cu, w.mask, w.scale)
         err = G.max_err(got, want)
     else:
+        group = w.n_q_heads // w.n_kv_heads
+        full_heads = np.arange(w.n_kv_heads) * group
+        T = w.total_tokens
+        rows = np.repeat(np.arange(T), full_heads.size)
+        heads = np.tile(full_heads, T)
+        want = orc.attention_rows(q, k, v, cu, w.mask, w.scale, rows, heads)
+        err = G.max_err(got[rows, heads], want)
+        assert err <= G.TOL[w.dtype], f"{name}: heads {full_heads.tolist()}, every row: {err:.3e}"
         rows, heads = _sample_rows(cu, w.n_q_heads, np.random.Generator(np.random.PCG64(5)))
         want = orc.attention_rows(q, k, v, cu, w.mask, w.scale, rows, heads)
         err = G.max_err(got[rows, heads], want)
