@@ -69,14 +69,19 @@ _LIB = None
 
 
 def load(path: str | None = None) -> "Oracle":
-    """An Oracle bound to ``path`` (default: the committed source, built on demand)."""
+    """An Oracle bound to ``path`` (default: the library $ATTN_ORACLE_LIBRARY names,
+    else the committed source, built on demand)."""
     global _LIB
     if path is not None:
         return Oracle(_bind(path))
     if _LIB is None:
-        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
-            build()
-        _LIB = _bind(LIBRARY)
+        override = os.environ.get("ATTN_ORACLE_LIBRARY")  # a prebuilt variant (e.g. sanitizer build)
+        if override:
+            _LIB = _bind(override)
+        else:
+            if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+                build()
+            _LIB = _bind(LIBRARY)
     return Oracle(_LIB)
 
 

@@ -46,14 +46,19 @@ _LIB = None
 
 
 def load(path: str | None = None) -> "GdnOracle":
-    """A GdnOracle bound to ``path`` (default: the committed source, built on demand)."""
+    """A GdnOracle bound to ``path`` (default: the library $GDN_ORACLE_LIBRARY names,
+    else the committed source, built on demand)."""
     global _LIB
     if path is not None:
         return GdnOracle(_bind(path))
     if _LIB is None:
-        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
-            build()
-        _LIB = _bind(LIBRARY)
+        override = os.environ.get("GDN_ORACLE_LIBRARY")  # a prebuilt variant (e.g. sanitizer build)
+        if override:
+            _LIB = _bind(override)
+        else:
+            if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+                build()
+            _LIB = _bind(LIBRARY)
     return GdnOracle(_LIB)
 
 
