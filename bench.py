@@ -12,12 +12,18 @@ over its growing cache (attn_prefill_kv); and decode (attn_decode) of one
 and of 64 newest tokens over 10240-token caches; the chunked gated delta rule
 (gdn_prefill) over the 10k sequence and the packed batch, 16 heads of 128;
 the QKV and output projections of the 10k sequence (int8 weights dequantized
-once, vendor bf16 GEMM).  Each of these is timed as >= 20 samples of R back-to-back calls (R chosen so
-a sample lasts >= 1 ms) between two events, reported per call as median /
-min / p90.  Prints ONE JSON line.
+once, vendor bf16 GEMM); the fixed-shape causal sweep N = 2048 ... 10240
+(16/2 heads, head dim 128) that judges the flat profile; and the 10k causal
+shape in fp32 against the fp32 matrix peak.  Each of these is timed as >= 20
+samples of R back-to-back calls (R chosen so a sample lasts >= 4 ms) between
+two events, reported per call as median / min / p90.  The headline's own
+timed region (W warmup calls, then exactly K calls between two events) runs
+after its sampled measurement, on a GPU whose clock has settled.  The fp64
+oracle is timed once on every workload on the host cores.  Prints ONE JSON
+line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only]
-                    [--no-cpu-baseline] [--sweep] [--copy-calibration]
+                    [--no-cpu-baseline] [--no-sweep] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -103,7 +109,13 @@ def time_calls(w, dev, cu, steps, warmup):
     return start.elapsed_time(end) / steps, out
 
 
-def sample_calls(w, dev, cu, n_samples=20, min_ms=1.0):
+# Samples last >= 4 ms of back-to-back calls: shorter ones, each followed by
+# a synchronisation, catch the clock boost an idle moment brings and read a few
+# per cent faster than sustained back-to-back calls.
+SAMPLE_MS = 4.0
+
+
+def sample_calls(w, dev, cu, n_samples=20, min_ms=SAMPLE_MS):
     """Per-call ms of n_samples samples of attn_prefill on the workload (see
     event_samples)."""
     import torch
@@ -134,7 +146,7 @@ def summarize(w, per_call_ms, reps):
     return res
 
 
-def event_samples(fn, n_samples=20, min_ms=1.0):
+def event_samples(fn, n_samples=20, min_ms=SAMPLE_MS):
     """Per-call ms of fn(): n_samples samples of R back-to-back calls between
     two events on the current stream, R chosen so a sample lasts >= min_ms."""
     import torch
@@ -391,49 +403,53 @@ def read_counters():
         return None
 
 
-def ordinal_suffix(n):
-    if n % 100 in (11, 12, 13):
-        return "th"
-    return {1: "st", 2: "nd", 3: "rd"}.get(n % 10, "th")
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo) and its logical CPU count."""
+    name = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return name, os.cpu_count()
 
 
-def cpu_baseline(w, host_inputs, target_s=12.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the workload's
-    rows (every head of strided rows), scaled to tokens/s by the share of
-    (query, key) pairs the sample covers."""
+def cpu_baseline():
+    """The fp64 oracle, as it stands, timed once end to end on every workload
+    (the seeded inputs the GPU receives), on the host's cores."""
     import oracle
 
+    from long_context_attention_prefill_amd import workloads as W
+
     orc = oracle.load()
-    q, k, v, cu = host_inputs
-    T, hq = w.total_tokens, w.n_q_heads
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-
-    def run(stride):
-        rows = np.arange(stride // 2, T, stride)
-        r = np.repeat(rows, hq)
-        h = np.tile(np.arange(hq), rows.size)
+    per = {}
+    for key in ("1", "2", "3", "4", "5a", "5b"):
+        w = W.WORKLOADS[key]
+        q, k, v, cu = W.make_inputs(w)
         t0 = time.perf_counter()
-        orc.attention_rows(q, k, v, cu, w.mask, w.scale, r, h)
+        orc.attention(q, k, v, cu, w.mask, w.scale)
         dt = time.perf_counter() - t0
-        assert w.mask == "causal" and len(w.seq_lens) == 1
-        sample_pairs = int(np.sum(rows + 1)) * hq
-        return dt, sample_pairs, rows.size
-
-    dt, sp, nrows = run(1024)
-    stride = max(1, int(1024 * dt / target_s))
-    if stride < 1024:
-        dt, sp, nrows = run(stride)
-    full_pairs = pairs_of(w) * hq
-    est_full_s = dt * full_pairs / sp
+        flops, _ = algorithmic(w)
+        per[key] = {"workload": w.name, "seconds": round(dt, 3),
+                    "tokens_per_s": round(w.total_tokens / dt, 1),
+                    "gflops_fp64": round(flops / dt / 1e9, 2)}
+    model, ncpu = cpu_model()
+    head = per["3"]
     return {
-        "value": T / est_full_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"fp64 C oracle (OpenMP, {threads} threads) on {nrows} rows x {hq} heads "
-                   f"(every {stride}{ordinal_suffix(stride)} query row), {sp / full_pairs:.4f} of the workload's "
-                   f"query-key pairs in {dt:.2f} s; scaled to the full workload: "
-                   f"{est_full_s:.1f} s"),
+        "sample": (f"the whole 10240-token causal workload (every row and head) through the fp64 C "
+                   f"oracle (OpenMP, {threads} threads) in {head['seconds']} s; every other "
+                   "workload timed once the same way (per_config)"),
+        "cpu_model": model,
+        "logical_cpus": ncpu,
+        "per_config": per,
     }
 
 
@@ -447,8 +463,8 @@ def main():
                     help="time only the 10k workload (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
-    ap.add_argument("--sweep", action="store_true",
-                    help="also print TFLOP/s for N = 2048..10240 (16/2 heads, causal)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the N = 2048..10240 sweep (16/2 heads, causal) and the fp32 line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -466,6 +482,8 @@ def main():
 
     w10 = W.WORKLOADS["3"]
     host10, dev10 = device_inputs(w10)
+    # the sampled measurement first: by the timed region the clock has settled
+    stats10 = None if args.headline_only else summarize(w10, *sample_calls(w10, dev10, host10[3]))
     ms10, out10 = time_calls(w10, dev10, host10[3], args.steps, args.warmup)
     flops10, bytes10 = algorithmic(w10)
     tflops10 = flops10 / (ms10 * 1e-3) / 1e12
@@ -477,10 +495,8 @@ def main():
         c = w10.needle_coords[h // G]
         assert int(np.argmax(last[h])) == c and last[h, c] >= 0.99, f"needle lost in head {h}"
 
-    stats10 = None
     others = {}
     if not args.headline_only:
-        stats10 = summarize(w10, *sample_calls(w10, dev10, host10[3]))
         others["chunked"] = chunked_prefill(w10, dev10, 2048)
         del dev10[:]
         for key in ("2", "4", "5a", "5b"):
@@ -504,15 +520,27 @@ def main():
         others["vision_f32"] = vision_step("vision_slices_f32")
         torch.cuda.empty_cache()
 
-    sweep = None
-    if args.sweep:
+    sweep = fp32_10k = None
+    if not args.no_sweep and not args.headline_only:
+        # fixed shape (16/2 heads, head dim 128, causal, bf16): the rate of the
+        # O(N^2) work from 2k to 10k tokens (median of sampled calls)
         sweep = {}
         for n in (2048, 4096, 6144, 8192, 10240):
             ws = W.Workload(f"sweep {n}", [0, n], 16, 2, 128, W.BF16, "causal", 1.0, seed=n)
             hs, ds = device_inputs(ws)
-            ms, _ = time_calls(ws, ds, hs[3], args.steps, args.warmup)
-            sweep[str(n)] = round(algorithmic(ws)[0] / (ms * 1e-3) / 1e12, 1)
+            per_call, _ = sample_calls(ws, ds, hs[3])
+            sweep[str(n)] = round(algorithmic(ws)[0] / (float(np.median(per_call)) * 1e-3) / 1e12, 1)
+            del ds
         sweep["flat_ratio_10k_over_2k"] = round(sweep["10240"] / sweep["2048"], 3)
+        sweep["pages_ratio_10k_over_2k"] = round(361.0 / 408.0, 3)
+        # the 10k causal shape in fp32 (the pages' own precision), fp32 matrix peak
+        wf = W.Workload("causal fp32 N=10240 16/2 heads d=128", [0, 10240], 16, 2, 128, W.F32,
+                        "causal", 0.5, seed=3)
+        hf, df = device_inputs(wf)
+        fp32_10k = summarize(wf, *sample_calls(wf, df, hf[3]))
+        fp32_10k["pct_fp32_peak"] = round(100 * fp32_10k["tflops"] / PEAK_F32_TFLOPS, 2)
+        del df
+        torch.cuda.empty_cache()
 
     if args.copy_calibration:
         # known traffic: 256 MiB read + 256 MiB written per copy kernel
@@ -566,8 +594,9 @@ def main():
         line["gpu_clock"] = gpu_clock()
     if sweep is not None:
         line["sweep_tflops_16x2_causal"] = sweep
+        line["fp32_causal_10k"] = fp32_10k
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w10, host10)
+        line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
 
 
