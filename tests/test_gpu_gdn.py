@@ -231,3 +231,36 @@ def test_gdn_long_state_in_place(gdn_orc):
     want0, _ = gdn_orc.gated_delta_rule(q, k, v, g, beta, cu, scale)
     got0, _ = _run(q, k, v, g, beta, cu, scale, want_state=False)
     _assert_close(got0, want0, "outputs without states")
+
+
+def _check_gates(gdn_orc, lens, H, seed, decays, with_s0=True):
+    """Like _check, with the decay of sequence b drawn from decays[b]: strong
+    gates (alpha down to 0.001) drive the cumulative log-gate of a 64-token
+    chunk far below fp32's exponent range, where only ratios of gates
+    (differences of log-gates) stay finite."""
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    q, k, v, g, beta = W.make_gdn_inputs(lens, H, 128, 128, seed)
+    rng = np.random.Generator(np.random.PCG64(seed + 1))
+    for b, (lo, hi) in enumerate(decays):
+        s, e = int(cu[b]), int(cu[b + 1])
+        alpha = rng.uniform(lo, hi, (e - s, H))
+        g[s:e] = W.round_to(np.log(alpha), W.F32)
+    scale = 1 / math.sqrt(128)
+    s0 = _state0(len(lens), H, seed + 100) if with_s0 else None
+    got, fin = _run(q, k, v, g, beta, cu, scale, s0=s0)
+    want, want_fin = gdn_orc.gated_delta_rule(q, k, v, g, beta, cu, scale, initial_state=s0)
+    _assert_close(got, want, f"outputs, decays {decays}")
+    _assert_close(fin, want_fin, f"final state, decays {decays}")
+
+
+@pytest.mark.parametrize("decay", [(0.01, 1.0), (0.001, 0.05)], ids=str)
+@pytest.mark.parametrize("lens", [[200], [37, 64, 130], [1000]], ids=str)
+def test_gdn_strong_decay(gdn_orc, lens, decay):
+    _check_gates(gdn_orc, lens, 2, seed=300 + sum(lens), decays=[decay] * len(lens))
+
+
+def test_gdn_mixed_strong_and_weak_gates(gdn_orc):
+    """One batch whose sequences alternate strong and weak gates."""
+    lens = [130, 200, 64, 300, 1]
+    decays = [(0.001, 0.05), (0.85, 1.0), (0.01, 1.0), (0.95, 1.0), (0.001, 0.01)]
+    _check_gates(gdn_orc, lens, 3, seed=400, decays=decays)
