@@ -148,6 +148,9 @@ int run(const void *q, const void *k, const void *v, void *out, float *lse,
       start += static_cast<int64_t>(a.seq_tiles[k - 1] - below) * static_cast<int64_t>(k) * n_q_heads;
     }
     a.level_start[cnt] = static_cast<int32_t>(start);  // == total_items
+    a.tickets = nullptr;
+    a.ticket_from = a.total_items;
+    if (bf16 && attn::work_tickets(a, stream) != 0) return ATTN_ELAUNCH;
     plan.push_back(a);
   }
   for (const attn::LaunchArgs &la : plan) {

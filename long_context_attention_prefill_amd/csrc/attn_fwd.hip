@@ -34,7 +34,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <set>
 #include <type_traits>
+#include <utility>
+#include <vector>
 
 #include "attn_device.h"
 #include "attn_launch.h"
@@ -175,7 +181,20 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  const Item it = decode_item(a, blockIdx.x);
+  // Item of this workgroup: its own index, or with work tickets (past the
+  // first wave) the next unclaimed item.
+  int item = blockIdx.x;
+  if (a.tickets != nullptr && item >= a.ticket_from) {
+    __shared__ int ticket;
+    if (tid == 0) ticket = a.ticket_from + atomicAdd(&a.tickets[0], 1);
+    __syncthreads();
+    item = ticket;
+  }
+  // a ticket past the last item (counters not at zero, which a launch that
+  // ran to completion never leaves) claims no work
+  const bool has_item = item < a.total_items;
+  if (!has_item) item = 0;
+  const Item it = decode_item(a, item);
   const int s0q = a.q_start[it.seq], s0k = a.k_start[it.seq];
   // queries are the last nq of nk positions: local row i sits at i + off
   const int nq = a.q_len[it.seq], nk = a.k_len[it.seq], off = nk - nq;
@@ -194,11 +213,12 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
   int kv_lo, kv_hi, tmp;
   row_range(mask, W, q0 + off, nk, kv_lo, tmp);
   row_range(mask, W, qend - 1 + off, nk, tmp, kv_hi);
+  if (!has_item) kv_hi = kv_lo;  // no tiles
 
   // The wave's rows [wq0, wq0 + 32R): the union of their visible keys is
   // [w_lo, w_hi), the intersection [i_lo, i_hi).
   const int wq0 = q0 + wave * 32 * R;
-  const bool wave_active = wq0 < nq;
+  const bool wave_active = has_item && wq0 < nq;
   int w_lo = 0, w_hi = 0, i_lo = 0, i_hi = 0;
   if (wave_active) {
     const int wq1 = min(wq0 + 32 * R, nq);
@@ -481,7 +501,7 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
     row_range(mask, W, q0 + off, nk, tmp2, whi);
     const int first = max(1, (wlo - kv_lo + BN - 1) / BN);
     const int last = max(0, (whi - kv_lo) / BN);  // tiles [0, last) end at or before whi
-    if (last > first) {
+    if (has_item && last > first) {
       t_plain0 = first;
       t_plain1 = last;
     }
@@ -651,6 +671,12 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
           }
       }
     }
+  }
+  // every workgroup counts itself out; the last one leaves the counters at
+  // zero for the stream's next launch
+  if (a.tickets != nullptr && tid == 0 && atomicAdd(&a.tickets[1], 1) == a.total_items - 1) {
+    atomicExch(&a.tickets[0], 0);
+    atomicExch(&a.tickets[1], 0);
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
@@ -851,8 +877,8 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_mfma(const LaunchArgs a) {
 template <typename K>
 int launch(K kernel, const LaunchArgs &a, int threads, void *stream) {
   void *args[] = {const_cast<LaunchArgs *>(&a)};
-  return static_cast<int>(hipLaunchKernel(reinterpret_cast<const void *>(kernel),
-                                          dim3(a.total_items), dim3(threads), args, 0,
+  return static_cast<int>(hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3(a.total_items),
+                                          dim3(threads), args, 0,
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -870,6 +896,84 @@ int launch_bf16(const LaunchArgs &a, int head_dim, void *stream) {
     case 128: return launch(fwd_bf16_fast<128, kWavesBf16, 1>, a, kWavesBf16 * 64, stream);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Work tickets.  The hardware hands workgroup b to XCD b mod 8, and each XCD
+// runs its share at its own pace: on a 10k-token causal launch the XCDs'
+// per-tile times differ by up to ~8 %, so with items bound to workgroups the
+// fast XCDs idle while the slowest finishes.  For heavy causal launches the
+// first wave of workgroups (one per slot) keeps items 0 .. slots-1, and every
+// later workgroup takes the next item, heaviest first, from a device counter
+// when it starts, whichever XCD it runs on: list scheduling over the whole
+// chip.  Each stream owns one pair of counters (ticket, finished) in a static
+// device array; launches on one stream run one after another, so they share
+// it, and the last workgroup of a launch puts both counters back to zero.
+// Streams under capture (whose graph may later replay beside eager launches
+// on the same stream) and the per-thread default stream (one handle, many
+// streams) launch without tickets, as does any stream once the array is full.
+// ---------------------------------------------------------------------------
+
+constexpr int kTicketSlots = 1024;  // streams per device
+static __device__ int32_t ticket_pool[2 * kTicketSlots];
+
+namespace {
+
+constexpr int kTicketDevices = 64;
+constexpr int kSlotsPerCu = 2;  // resident workgroups of the bf16 kernel
+
+struct DeviceTickets {
+  int32_t *pool = nullptr;
+  int slots = 0;  // workgroup slots of the device
+  std::map<hipStream_t, int> owner;
+};
+std::mutex ticket_mutex;
+DeviceTickets device_tickets[kTicketDevices];
+
+}  // namespace
+
+int work_tickets(LaunchArgs &a, void *stream) {
+  a.tickets = nullptr;
+  a.ticket_from = a.total_items;
+  if (a.mask_kind != kCausal) return 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (st == hipStreamPerThread) return 0;
+  int dev = 0;
+  hipError_t e = st != nullptr ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return static_cast<int>(e);
+  if (dev < 0 || dev >= kTicketDevices) return 0;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if ((e = hipStreamIsCapturing(st, &cs)) != hipSuccess) return static_cast<int>(e);
+  if (cs != hipStreamCaptureStatusNone) return 0;
+  std::lock_guard<std::mutex> lock(ticket_mutex);
+  DeviceTickets &dt = device_tickets[dev];
+  if (dt.pool == nullptr) {
+    int cur = 0, cus = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return static_cast<int>(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return static_cast<int>(e);
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(ticket_pool));
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return static_cast<int>(e);
+    if (p == nullptr || cus <= 0) return static_cast<int>(hipErrorInvalidSymbol);
+    dt.pool = static_cast<int32_t *>(p);
+    dt.slots = kSlotsPerCu * cus;
+  }
+  // with a few items per slot the static heaviest-first order already
+  // balances, and a ticket's round trip would only lengthen each item
+  if (a.total_items <= 2 * dt.slots) return 0;
+  auto it = dt.owner.find(st);
+  if (it == dt.owner.end()) {
+    if (static_cast<int>(dt.owner.size()) >= kTicketSlots) return 0;
+    it = dt.owner.emplace(st, static_cast<int>(dt.owner.size())).first;
+  }
+  a.tickets = dt.pool + 2 * it->second;
+  a.ticket_from = dt.slots;
+  return 0;
 }
 
 int launch_f32(const LaunchArgs &a, int head_dim, void *stream) {

@@ -47,6 +47,12 @@ struct LaunchArgs {
   // and their items start at level_start[k-1]; level_start[n_seqs] =
   // total_items (seq_tiles[n_seqs] reads as 0).
   int32_t level_start[kMaxSeqsPerLaunch + 1];
+  // Work tickets (device, two counters at zero), or null: workgroup b runs
+  // item b of the order above if b < ticket_from, else item ticket_from +
+  // tickets[0]++ claimed when it starts; tickets[1] counts finished
+  // workgroups, and the last one puts both back to zero.
+  int32_t *tickets;
+  int32_t ticket_from;
 };
 
 // Decode: one query (the newest token) per sequence against its key/value
@@ -108,5 +114,13 @@ int decode_scratch(void *stream, void **ptr);
 // Query rows per workgroup of each family (the planner tiles with it).
 int rows_per_workgroup_bf16(int head_dim);
 int rows_per_workgroup_f32(int head_dim);
+
+// For a causal bf16 launch with many more items than workgroup slots: point
+// a.tickets at the stream's counters (a static device array, one pair per
+// stream and device) and set a.ticket_from to the device's workgroup slots;
+// leaves a.tickets null (items bound to workgroups) on other launches, a
+// stream under capture, the per-thread default stream, or a full array.
+// 0 or a hipError_t.
+int work_tickets(LaunchArgs &a, void *stream);
 
 }  // namespace attn

@@ -19,6 +19,11 @@ int decode_scratch(void *, void **ptr) {
   *ptr = nullptr;
   return 1;
 }
+int work_tickets(LaunchArgs &a, void *) {
+  a.tickets = nullptr;
+  a.ticket_from = a.total_items;
+  return 0;
+}
 }  // namespace attn
 
 namespace gdn {
