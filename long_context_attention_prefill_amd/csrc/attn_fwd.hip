@@ -650,26 +650,51 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
   }
 
   if (wave_active) {
+    // Output rows go through LDS (the wave's own 32 rows of the K buffers,
+    // free once the sweep is over): the accumulator holds 4-column pieces of
+    // 32 rows, and read back, consecutive lanes hold consecutive 16-byte
+    // chunks of whole rows, so each store writes whole rows (for head_dim
+    // 128, four 256-byte rows).  head_dim 128 stages row i's chunk c at slot
+    // c ^ (i mod 16) (no conflicts on the reads, 2-way on the writes); 64 and
+    // 72 pad each staged row by one chunk.
+    constexpr int CHR = D / 8;                    // 16-byte chunks per output row
+    constexpr int SR = XOR ? D * 2 : D * 2 + 16;  // bytes per staged row
+    static_assert(2 * 32 * SR <= BUF_BYTES, "two waves' staged rows fit one K buffer");
+    char *stage = (wave < 2 ? k_lds0 : k_lds1) + (wave & 1) * 32 * SR;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float l_tot = l_run[r] + xor32(l_run[r]);
-      if (row_ok[r]) {
-        const float inv = 1.0f / l_tot;
-        if (a.lse != nullptr && g == 0)
-          a.lse[(size_t)(s0q + row[r]) * a.hq + h] = (m_ref[r] + log2f(l_tot)) * kLn2;
-        __bf16 *orow = reinterpret_cast<__bf16 *>(a.out) + ((size_t)(s0q + row[r]) * a.hq + h) * D;
+      const float inv = row_ok[r] ? 1.0f / l_tot : 0.0f;
+      if (row_ok[r] && a.lse != nullptr && g == 0)
+        a.lse[(size_t)(s0q + row[r]) * a.hq + h] = (m_ref[r] + log2f(l_tot)) * kLn2;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int d = 32 * db + 8 * jj + 4 * g;
-            if (d >= D) continue;  // padding rows of O^T
-            bf16x4 w;
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d = 32 * db + 8 * jj + 4 * g;
+          if (d >= D) continue;  // padding rows of O^T
+          bf16x4 w;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[r][db][4 * jj + e] * inv);
-            *reinterpret_cast<bf16x4 *>(orow + d) = w;
-          }
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[r][db][4 * jj + e] * inv);
+          const int off = XOR ? (((d >> 3) ^ (l32 & 15)) << 4) + 8 * g : 2 * d;
+          *reinterpret_cast<bf16x4 *>(stage + l32 * SR + off) = w;
+        }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the staged rows are in LDS
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < (32 * CHR + 63) / 64; ++i) {
+        const int f = 64 * i + lane;
+        const int sr = f / CHR, cc = f - sr * CHR;
+        const int qr = wq0 + 32 * r + sr;
+        if (sr < 32 && qr < nq) {
+          const int off = XOR ? ((cc ^ (sr & 15)) << 4) : 16 * cc;
+          const bf16x8 val = *reinterpret_cast<const bf16x8 *>(stage + sr * SR + off);
+          *reinterpret_cast<bf16x8 *>(reinterpret_cast<__bf16 *>(a.out) + ((size_t)(s0q + qr) * a.hq + h) * D +
+                                      8 * cc) = val;
+        }
       }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next sub-block's writes
+      __builtin_amdgcn_wave_barrier();
     }
   }
   // every workgroup counts itself out; the last one leaves the counters at
