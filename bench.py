@@ -18,8 +18,8 @@ shape in fp32 against the fp32 matrix peak.  Each of these is timed as >= 20
 samples of R back-to-back calls (R chosen so a sample lasts >= 4 ms) between
 two events, reported per call as median / min / p90; the headline's samples
 are instead 20 runs of its own timed protocol (W warmup calls, a
-synchronisation, then exactly K calls between two events), and its timed
-region is one more run of it.  The fp64
+synchronisation, then exactly K calls between two events), 10 before and 10
+after its timed region, which is one more run of it.  The fp64
 oracle is timed once on every workload on the host cores.  Prints ONE JSON
 line.
 
@@ -484,19 +484,25 @@ def main():
     w10 = W.WORKLOADS["3"]
     host10, dev10 = device_inputs(w10)
     # The headline's samples are 20 runs of the timed protocol itself (W
-    # warmup calls, a synchronisation, K back-to-back calls); the timed region
-    # is one more.  Both therefore see the same clock behaviour: after an idle
-    # moment the GPU's power management holds back the first ~100 ms of load,
-    # and back-to-back calls with no gap run a few per cent slower than short
-    # bursts between synchronisations.
+    # warmup calls, a synchronisation, K back-to-back calls), 10 before and
+    # 10 after the timed region, which is one more run in their middle.  Both
+    # therefore see the same clock behaviour: after an idle moment the GPU's
+    # power management holds back the first ~100 ms of load, back-to-back
+    # calls with no gap run a few per cent slower than short bursts between
+    # synchronisations, and the clock drifts under sustained load.
+    def protocol_windows(n):
+        return [time_calls(w10, dev10, host10[3], args.steps, args.warmup)[0] for _ in range(n)]
+
+    before = [] if args.headline_only else protocol_windows(10)
+    ms10, out10 = time_calls(w10, dev10, host10[3], args.steps, args.warmup)
     if args.headline_only:
         stats10 = None
     else:
-        windows = np.array([time_calls(w10, dev10, host10[3], args.steps, args.warmup)[0]
-                            for _ in range(20)])
+        windows = np.array(before + protocol_windows(10))
         stats10 = summarize(w10, windows, args.steps)
-        stats10["protocol"] = f"20 windows of {args.warmup} warmup + {args.steps} timed calls"
-    ms10, out10 = time_calls(w10, dev10, host10[3], args.steps, args.warmup)
+        stats10["protocol"] = (f"20 windows of {args.warmup} warmup + {args.steps} timed calls, "
+                               "10 before and 10 after the timed region")
+        stats10["windows_ms"] = [round(float(x), 5) for x in windows]
     flops10, bytes10 = algorithmic(w10)
     tflops10 = flops10 / (ms10 * 1e-3) / 1e12
 
