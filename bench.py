@@ -591,7 +591,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops10, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops10 / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "counters": counters,
-                     "kernel": "fwd_bf16_fast<128,4,1>", "algorithmic_flops": flops10,
+                     "kernel": "fwd_bf16_fast<128,4,1,64>", "algorithmic_flops": flops10,
                      "algorithmic_bytes": bytes10},
     }
     if stats10 is not None:

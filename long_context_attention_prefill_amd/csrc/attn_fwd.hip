@@ -132,9 +132,12 @@ __device__ __forceinline__ void row_range(int mask, int W, int i, int n, int &lo
 // (one wave per SIMD, up to 512 registers) halves the LDS reads and K/V tile
 // loads per MFMA, but with no second wave to hide latency and its scores
 // spilling into AGPRs it measured ~30 % slower on gfx950, so it is not
-// instantiated.
-template <int D, int NW, int R>
-__global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs a) {
+// instantiated.  BN is the key tile: 64 keys, or at head_dim 128 32 keys,
+// which halves the LDS buffers (32 KB per workgroup) and the scores' and
+// probabilities' registers (168 VGPRs), so three workgroups fit on a CU
+// (three waves per SIMD).
+template <int D, int NW, int R, int BN>
+__global__ __launch_bounds__(NW * 64, BN == 32 ? 3 : 2 / R) void fwd_bf16_fast(const LaunchArgs a) {
   // The host pass only needs this kernel's signature for its launch stub;
   // the body (gfx950-only builtins) is compiled for the device alone.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -142,7 +145,8 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
   static_assert(R == 1 || R == 2, "one or two query sub-blocks per wave");
   using L = FastLayout<D>;
   constexpr int BM = NW * 32 * R;
-  constexpr int BN = 64;
+  static_assert(BN == 64 || (BN == 32 && D == 128 && R == 1), "64-key tiles, or 32-key tiles at head_dim 128");
+  constexpr int NB = BN / 32;  // 32-key blocks of S^T per tile
   constexpr int CH = L::CH;
   constexpr int KST = L::KST;         // MFMA k steps of S^T (the last one zero-padded when D = 72)
   constexpr int DB = (D + 31) / 32;  // 32-row blocks of O^T (rows past D are computed and dropped)
@@ -368,10 +372,10 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
 
   // S^T = K Q^T for the 64 keys held in K buffer KB, every sub-block; each K
   // fragment feeds the R sub-blocks' MFMAs in a row.
-  auto qk = [&](auto kbuf_tag, f32x16 (&sc)[R][2]) {
+  auto qk = [&](auto kbuf_tag, f32x16 (&sc)[R][NB]) {
     const char *kb = k_buf(kbuf_tag);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int r = 0; r < R; ++r) sc[r][nb] = (f32x16)(0.0f);
 #pragma unroll
@@ -392,6 +396,32 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
   // per MFMA measured 0.7 % faster at 10k and 3-7 % at 1-2k tokens) (mask:
   // 2 VALU, 8 MFMA, 0x20 VMEM read, 0x100 DS read).
   auto plain_tile_schedule = [&]() {
+    if constexpr (NB == 1) {
+      // 32-key tiles: S^T with the next tile's loads, the softmax of the
+      // first k step, the PV MFMAs of that k step under the softmax of the
+      // second, then the second k step's PV
+      constexpr int SV = 24;  // VALU ops of one k step's softmax
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < KST; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x002, SV, 0);
+#pragma unroll
+      for (int i = 0; i < DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, SV / DB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < DB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      return;
+    }
     constexpr int SOFT = 3 * (BN / 2) / KST;  // softmax VALU ops per QK MFMA
     constexpr int PV_HALF = DB * (BN / 32);   // PV k-step pairs' fragments
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -419,25 +449,25 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
       if (i % R == R - 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
-  auto apply_mask = [&](f32x16 (&sc)[R][2], int kt) {
+  auto apply_mask = [&](f32x16 (&sc)[R][NB], int kt) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) sc[r][nb][j] = visible(r, kt, nb, j) ? sc[r][nb][j] : s_void;
   };
   // Row maximum of c*s over the tile for sub-block r, both lane halves combined.
-  auto row_max = [&](const f32x16 (&scr)[2]) {
+  auto row_max = [&](const f32x16 (&scr)[NB]) {
     float mx = kNegInf;
     if (neg) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = fmaxf(mx, -scr[nb][j]);
     } else {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = fmaxf(mx, scr[nb][j]);
     }
@@ -448,7 +478,7 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
   // of those same bf16 values.  k step ks covers keys 16ks .. 16ks+15, held
   // in accumulator entries 8*(ks&1) .. +7 of block ks>>1; entry e of lane
   // half g is key 16ks + g + 4(e & 3) + 2(e >> 2).
-  auto softmax = [&](f32x16 (&sc)[R][2], bf16x8 (&pf)[R][BN / 16]) {
+  auto softmax = [&](f32x16 (&sc)[R][NB], bf16x8 (&pf)[R][BN / 16]) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int ks = 0; ks < BN / 16; ++ks)
@@ -525,11 +555,11 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
       }
     }
     if (wave_sees(t)) {
-      f32x16 sc[R][2];
+      f32x16 sc[R][NB];
       {
         const char *kb = k_rt(buf);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
           for (int r = 0; r < R; ++r) sc[r][nb] = (f32x16)(0.0f);
 #pragma unroll
@@ -574,7 +604,7 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
     const int kn = min(kt + BN, kv_hi);
     issue_k(kn, std::integral_constant<int, BUF ^ 1>{});
     issue_v(kn, std::integral_constant<int, BUF ^ 1>{});
-    f32x16 sc[R][2];
+    f32x16 sc[R][NB];
     bf16x8 pf[R][BN / 16];
     qk(buf_tag, sc);
     softmax(sc, pf);
@@ -607,7 +637,7 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
       const int kt = kv_lo + t * BN;
       issue_k(min(kt + BN, kv_hi), std::integral_constant<int, BUF ^ 1>{});
       if (wave_sees(t)) {
-        f32x16 sc[R][2];
+        f32x16 sc[R][NB];
         qk(buf_tag, sc);
         if (needs_mask(t)) apply_mask(sc, kt);
 #pragma unroll
@@ -659,8 +689,13 @@ __global__ __launch_bounds__(NW * 64, 2 / R) void fwd_bf16_fast(const LaunchArgs
     // 72 pad each staged row by one chunk.
     constexpr int CHR = D / 8;                    // 16-byte chunks per output row
     constexpr int SR = XOR ? D * 2 : D * 2 + 16;  // bytes per staged row
-    static_assert(2 * 32 * SR <= BUF_BYTES, "two waves' staged rows fit one K buffer");
-    char *stage = (wave < 2 ? k_lds0 : k_lds1) + (wave & 1) * 32 * SR;
+    char *stage;
+    if constexpr (2 * 32 * SR <= BUF_BYTES) {
+      stage = (wave < 2 ? k_lds0 : k_lds1) + (wave & 1) * 32 * SR;
+    } else {  // 32-key tiles: one wave per K or V buffer
+      static_assert(NW == 4 && 32 * SR <= BUF_BYTES, "a wave's staged rows fit one buffer");
+      stage = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float l_tot = l_run[r] + xor32(l_run[r]);
@@ -908,6 +943,12 @@ int launch(K kernel, const LaunchArgs &a, int threads, void *stream) {
 }
 
 constexpr int kWavesBf16 = 4;
+// head_dim 128 launches of at least this many items (12 rounds of 256 CUs'
+// workgroups) take 32-key tiles at three workgroups per CU: the third
+// workgroup hides more of each item's fixed costs (packed window-256 batch
+// -11 %, packed causal batch -2 %) while 64-key tiles run a launch of fewer,
+// longer items faster (10k causal +2 %, 2k causal +2 % with 32-key tiles)
+constexpr int kManyItems = 3072;
 
 }  // namespace
 
@@ -916,9 +957,12 @@ int rows_per_workgroup_f32(int) { return 128; }
 
 int launch_bf16(const LaunchArgs &a, int head_dim, void *stream) {
   switch (head_dim) {
-    case 64: return launch(fwd_bf16_fast<64, kWavesBf16, 1>, a, kWavesBf16 * 64, stream);
-    case 72: return launch(fwd_bf16_fast<72, kWavesBf16, 1>, a, kWavesBf16 * 64, stream);
-    case 128: return launch(fwd_bf16_fast<128, kWavesBf16, 1>, a, kWavesBf16 * 64, stream);
+    case 64: return launch(fwd_bf16_fast<64, kWavesBf16, 1, 64>, a, kWavesBf16 * 64, stream);
+    case 72: return launch(fwd_bf16_fast<72, kWavesBf16, 1, 64>, a, kWavesBf16 * 64, stream);
+    case 128:
+      return a.total_items >= kManyItems
+                 ? launch(fwd_bf16_fast<128, kWavesBf16, 1, 32>, a, kWavesBf16 * 64, stream)
+                 : launch(fwd_bf16_fast<128, kWavesBf16, 1, 64>, a, kWavesBf16 * 64, stream);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
 }
