@@ -87,3 +87,21 @@ def test_many_items_probe_index(mask, cu, hq, hkv, sign):
     q, k, v = W.probe_index_inputs(cu, hq, hkv, D, sign)
     got = G.run_hip(q, k, v, cu, mask, 1 / math.sqrt(D), "bf16")
     probes.check_index_output(got, cu, mask, hq, hkv, sign)
+
+
+def test_many_items_kv_with_lse(orc):
+    """Queries ending longer key sequences, with the log-sum-exp, at 3000+ items."""
+    lens_q = [6000, 5000, 0, 8800, 1]
+    lens_k = [6000, 5600, 300, 9000, 900]
+    cu_q, cu_k = np.cumsum([0] + lens_q), np.cumsum([0] + lens_k)
+    hq, hkv = 32, 4
+    assert _items(cu_q, hq) >= 3072
+    rng = np.random.Generator(np.random.PCG64(83))
+    q = W.round_to(rng.standard_normal((int(cu_q[-1]), hq, D)), W.BF16)
+    k = W.round_to(rng.standard_normal((int(cu_k[-1]), hkv, D)), W.BF16)
+    v = W.round_to(rng.standard_normal((int(cu_k[-1]), hkv, D)), W.BF16)
+    mask = ("window", 96)
+    got, got_lse = G.run_hip_kv(q, k, v, cu_q, cu_k, mask, 1 / math.sqrt(D), "bf16", lse=True)
+    want, want_lse = orc.attention(q, k, v, cu_q, mask, 1 / math.sqrt(D), return_lse=True, cu_seqlens_k=cu_k)
+    assert G.max_err(got, want) <= G.TOL["bf16"]
+    assert G.max_err(got_lse, want_lse) <= G.LSE_TOL["bf16"]
