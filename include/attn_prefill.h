@@ -33,14 +33,21 @@
  * products, fp32 sums).
  *
  * Ownership: the caller owns every buffer.  cu_seqlens is a HOST array read
- * only during the call.  The library allocates no device memory, holds no
- * per-call state and may be called from several threads on several streams.
+ * only during the call.  The library allocates no device memory and may be
+ * called from several threads on several streams.  Its only state is a pair
+ * of work counters per stream and device, in a static device array that
+ * comes with the library's code (causal bf16 launches of more than two items
+ * per workgroup slot hand out their later items through them; each launch
+ * leaves them at zero).  Launches on a stream under capture, on the
+ * per-thread default stream, or on streams beyond the array's 1024 run
+ * without them.
  *
  * Execution: stream-ordered and asynchronous.  The call validates its
  * arguments on the host, enqueues its kernel(s) on `stream` (a hipStream_t;
  * NULL is the default stream) and returns; `out` is ready when the stream has
  * reached that point.  Results are deterministic: the same inputs give the
- * same bits.
+ * same bits (the work counters change which workgroup computes an item, not
+ * what it computes).
  *
  * Errors: every argument is checked before any device work; on error nothing
  * is enqueued and `out` is untouched.  No C++ exception crosses the ABI.
