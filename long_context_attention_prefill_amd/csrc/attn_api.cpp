@@ -120,13 +120,48 @@ int run(const void *q, const void *k, const void *v, void *out, float *lse,
   a.mask_kind = mask_kind;
   a.window = mask_kind == ATTN_WINDOW ? window : 0;
   a.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
-  a.bm = bm;
 
   // plan every launch before enqueuing any, so a rejected plan leaves no work behind
   std::vector<attn::LaunchArgs> plan;
   for (size_t base = 0; base < order.size(); base += attn::kMaxSeqsPerLaunch) {
     const size_t cnt = std::min(order.size() - base, static_cast<size_t>(attn::kMaxSeqsPerLaunch));
-    int64_t items = 0;
+    // bf16 launches of few items take key halves: half-height items whose two
+    // pairs of waves sweep the two halves of the keys (twice the workgroups).
+    // That pays when the items leave CUs idle, or when they are unequal (the
+    // longest item sets the time: causal tiles over a short prefix); equal
+    // items that already fill the CUs run as fast on whole rows.
+    int64_t items = 0, key_sum = 0, key_max = 0, max_keys = 0;
+    for (size_t i = 0; i < cnt; ++i) {
+      const int32_t b = order[base + i];
+      items += static_cast<int64_t>((nq(b) + bm - 1) / bm) * n_q_heads;
+      max_keys = std::max<int64_t>(max_keys, cu_k[b + 1] - cu_k[b]);
+    }
+    if (bf16 && items <= attn::kKeyHalvesMaxItems) {
+      for (size_t i = 0; i < cnt; ++i) {
+        const int32_t b = order[base + i];
+        const int64_t n_q = nq(b), n_k = cu_k[b + 1] - cu_k[b], offk = n_k - n_q;
+        for (int64_t q0 = 0; q0 < n_q; q0 += bm) {
+          const int64_t q1 = std::min<int64_t>(q0 + bm, n_q) - 1 + offk;  // last row's position
+          int64_t lo = 0, hi = n_k;  // keys of the tile's rows
+          if (mask_kind == ATTN_CAUSAL) {
+            hi = q1 + 1;
+          } else if (mask_kind == ATTN_WINDOW) {
+            lo = ((q0 + offk) / window) * window;
+            hi = std::min<int64_t>((q1 / window) * window + window, n_k);
+          }
+          key_sum += hi - lo;
+          key_max = std::max(key_max, hi - lo);
+        }
+      }
+    }
+    const bool few = items <= attn::kKeyHalvesFewItems;
+    const bool unequal = items <= attn::kKeyHalvesMaxItems && 2 * key_max * items >= 3 * key_sum * n_q_heads;
+    // (the kernel's buffer offsets into one head's keys stay below 2^31 bytes)
+    const bool halves = bf16 && (few || unequal) && max_keys * a.kv_stride * 2 < (int64_t{1} << 30);
+    const int bm_l = halves ? attn::rows_per_workgroup_bf16_halves(head_dim) : bm;
+    a.bm = bm_l;
+    a.key_halves = halves ? 1 : 0;
+    items = 0;
     a.n_seqs = static_cast<int32_t>(cnt);
     for (size_t i = 0; i < cnt; ++i) {
       const int32_t b = order[base + i];
@@ -134,7 +169,7 @@ int run(const void *q, const void *k, const void *v, void *out, float *lse,
       a.q_len[i] = nq(b);
       a.k_start[i] = cu_k[b];
       a.k_len[i] = cu_k[b + 1] - cu_k[b];
-      a.seq_tiles[i] = (a.q_len[i] + bm - 1) / bm;
+      a.seq_tiles[i] = (a.q_len[i] + bm_l - 1) / bm_l;
       items += static_cast<int64_t>(a.seq_tiles[i]) * n_q_heads;
     }
     if (items > INT32_MAX) return ATTN_EUNSUPPORTED;

@@ -136,17 +136,30 @@ __device__ __forceinline__ void row_range(int mask, int W, int i, int n, int &lo
 // which halves the LDS buffers (32 KB per workgroup) and the scores' and
 // probabilities' registers (168 VGPRs), so three workgroups fit on a CU
 // (three waves per SIMD).
-template <int D, int NW, int R, int BN>
-__global__ __launch_bounds__(NW * 64, BN == 32 ? 3 : 2 / R) void fwd_bf16_fast(const LaunchArgs a) {
+//
+// SPLIT (key halves, for launches too small to fill the GPU): a workgroup
+// covers 64 query rows, and its waves split the keys instead of the rows --
+// waves 0 and 1 (rows 0-31, 32-63) sweep the first half of the key tiles,
+// waves 2 and 3 (the same rows) the second half, in step: each LDS tile holds
+// BN = 32 keys of each half (one 64-key tile's space), and every wave computes
+// on its own half's 32 keys.  At the end waves 2 and 3 hand their rows'
+// references, sums and unnormalised outputs to waves 0 and 1 through LDS,
+// which fold them in (the merge of two softmax partitions) and store.  Twice
+// the workgroups of the plain split by rows, each half as long.
+template <int D, int NW, int R, int BN, bool SPLIT>
+__global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_bf16_fast(const LaunchArgs a) {
   // The host pass only needs this kernel's signature for its launch stub;
   // the body (gfx950-only builtins) is compiled for the device alone.
 #if defined(__HIP_DEVICE_COMPILE__)
   static_assert(D == 64 || D == 72 || D == 128, "fast path covers head_dim 64, 72 and 128");
   static_assert(R == 1 || R == 2, "one or two query sub-blocks per wave");
   using L = FastLayout<D>;
-  constexpr int BM = NW * 32 * R;
-  static_assert(BN == 64 || (BN == 32 && D == 128 && R == 1), "64-key tiles, or 32-key tiles at head_dim 128");
-  constexpr int NB = BN / 32;  // 32-key blocks of S^T per tile
+  static_assert(BN == 64 || (BN == 32 && R == 1 && (D == 128 || SPLIT)),
+                "64-key tiles, or 32-key tiles at head_dim 128 or with key halves");
+  static_assert(!SPLIT || (BN == 32 && R == 1 && NW == 4), "key halves: four waves, 32-key steps");
+  constexpr int HALVES = SPLIT ? 2 : 1;
+  constexpr int BM = NW * 32 * R / HALVES;  // query rows per workgroup
+  constexpr int NB = BN / 32;  // 32-key blocks of S^T per wave and tile
   constexpr int CH = L::CH;
   constexpr int KST = L::KST;         // MFMA k steps of S^T (the last one zero-padded when D = 72)
   constexpr int DB = (D + 31) / 32;  // 32-row blocks of O^T (rows past D are computed and dropped)
@@ -154,7 +167,7 @@ __global__ __launch_bounds__(NW * 64, BN == 32 ? 3 : 2 / R) void fwd_bf16_fast(c
   // slot c ^ (key mod 16) (the XOR layout); 64 and 72: the padded layout
   constexpr bool XOR = D == 128;
   constexpr int ROWB = XOR ? D * 2 : L::ROWB;  // bytes per key row in LDS
-  constexpr int KBUF = BN * ROWB;  // bytes per K (or V) tile
+  constexpr int KBUF = HALVES * BN * ROWB;  // bytes per K (or V) LDS tile (both halves)
   // A tile is NLOADS wave-wide direct loads (64 lanes x 16 bytes); each wave
   // issues NL of them, and a wave whose last load falls past the tile sends
   // it, all lanes out of range, into a 1 KB spill slot after the tile, so
@@ -182,6 +195,7 @@ __global__ __launch_bounds__(NW * 64, BN == 32 ? 3 : 2 / R) void fwd_bf16_fast(c
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   __builtin_assume(wave >= 0 && wave < NW);
+  const int half = SPLIT ? wave >> 1 : 0;  // key half this wave sweeps
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
@@ -221,7 +235,7 @@ __global__ __launch_bounds__(NW * 64, BN == 32 ? 3 : 2 / R) void fwd_bf16_fast(c
 
   // The wave's rows [wq0, wq0 + 32R): the union of their visible keys is
   // [w_lo, w_hi), the intersection [i_lo, i_hi).
-  const int wq0 = q0 + wave * 32 * R;
+  const int wq0 = q0 + (SPLIT ? 32 * (wave & 1) : wave * 32 * R);
   const bool wave_active = has_item && wq0 < nq;
   int w_lo = 0, w_hi = 0, i_lo = 0, i_hi = 0;
   if (wave_active) {
@@ -258,27 +272,38 @@ __global__ __launch_bounds__(NW * 64, BN == 32 ? 3 : 2 / R) void fwd_bf16_fast(c
   // Padded layout: slot p is row p / SLOTS, chunk p % SLOTS (chunks >= CH are
   // padding).  XOR layout: load j fills keys 4j .. 4j+3, lane l writing key
   // 4j + (l >> 4), slot l & 15, which holds chunk (l & 15) ^ (key & 15).
+  // Key halves: LDS rows BN .. 2BN-1 hold the second half's tile, ntiles
+  // tiles after the first half's, so their loads reach (ntiles - 1) BN rows
+  // further than their LDS row.
   const int rowbytes = a.kv_stride * 2;  // bytes between consecutive tokens of one head
+  const int n_key_tiles = (kv_hi - kv_lo + BN - 1) / BN;
+  const int ntiles = SPLIT ? (n_key_tiles + 1) / 2 : n_key_tiles;  // steps of a sweep
+  const int kv_w = kv_lo + half * ntiles * BN;  // first key of this wave's half
+  const uint32_t b_shift = SPLIT ? (uint32_t)((ntiles - 1) * BN * rowbytes) : 0u;
   uint32_t ld_off[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     if constexpr (XOR) {
       const int key = 4 * (wave + NW * i) + (lane >> 4);
-      ld_off[i] = (uint32_t)(key * rowbytes + ((lane & 15) ^ (key & 15)) * 16);
+      ld_off[i] = key < HALVES * BN ? (uint32_t)(key * rowbytes + ((lane & 15) ^ (key & 15)) * 16) +
+                                          (key >= BN ? b_shift : 0u)
+                                    : kOutOfRange;
     } else {
       const int p = (wave + NW * i) * 64 + lane;
       const int rr = p / L::SLOTS, cs = p % L::SLOTS;
-      ld_off[i] = cs < CH ? (uint32_t)(rr * rowbytes + cs * 16) : kOutOfRange;
+      ld_off[i] = cs < CH && rr < HALVES * BN ? (uint32_t)(rr * rowbytes + cs * 16) + (rr >= BN ? b_shift : 0u)
+                                              : kOutOfRange;
     }
   }
   const char *kseq = reinterpret_cast<const char *>(a.k) + ((size_t)s0k * a.kv_stride + (size_t)hk * D) * 2;
   const char *vseq = reinterpret_cast<const char *>(a.v) + ((size_t)s0k * a.kv_stride + (size_t)hk * D) * 2;
 
-  // Direct loads of the K (or V) rows kt .. kt+63 into an LDS buffer.
+  // Direct loads of the K (or V) rows kt .. kt+BN-1 (and with key halves the
+  // second half's rows, ntiles tiles on) into an LDS buffer.
   // kt >= kv_hi is allowed: the range is then empty, nothing is fetched and
   // the (unused) buffer fills with zeros, so a step needs no branch.
   auto issue = [&](const char *seq, char *lds, int kt) {
-    const int nrows = min(kv_hi - kt, BN);
+    const int nrows = SPLIT ? kv_hi - kt : min(kv_hi - kt, BN);
     const int rec = max(0, (nrows - 1) * rowbytes + D * 2);  // later rows read as zeros
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char *>(seq + (size_t)kt * rowbytes), (short)0, rec, kBufferWord3);
@@ -297,8 +322,9 @@ __global__ __launch_bounds__(NW * 64, BN == 32 ? 3 : 2 / R) void fwd_bf16_fast(c
   //   second half of a k step, +16 per k step) and columns
   //   32db + 16*(lane>>4 & 1) + 4q .. +3; the transpose hands lane j of the
   //   group column j of those four keys, in the order P holds them.
-  const int kread = key_of_row(l32) * ROWB + 16 * g;
-  const int vread = (g + 4 * ((lane & 15) >> 2)) * ROWB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+  const int hb = half * BN * ROWB;  // this wave's half of an LDS tile
+  const int kread = key_of_row(l32) * ROWB + 16 * g + hb;
+  const int vread = (g + 4 * ((lane & 15) >> 2)) * ROWB + 32 * ((lane >> 4) & 1) + 8 * (lane & 3) + hb;
   // XOR layout: chunk 2kk + g of key k sits at slot (2kk + g) ^ (k & 15), i.e.
   // at kaddr ^ 32 kk; the V chunk a lane reads for block db (and for the
   // second half of a k step, two keys on) sits at its db = 0 slot XOR 4 db
@@ -306,12 +332,12 @@ __global__ __launch_bounds__(NW * 64, BN == 32 ? 3 : 2 / R) void fwd_bf16_fast(c
   uint32_t kaddr[XOR ? KST : 1], vaddr[XOR ? DB : 1][2];
   if constexpr (XOR) {
     const int key = key_of_row(l32);
-    const int k0 = key * ROWB + ((g ^ (key & 1)) | (key & 14)) * 16;
+    const int k0 = key * ROWB + ((g ^ (key & 1)) | (key & 14)) * 16 + hb;
 #pragma unroll
     for (int kk = 0; kk < KST; ++kk) kaddr[kk] = (uint32_t)(k0 ^ (32 * kk));
-    const int r4 = (lane & 15) >> 2, q4 = lane & 3, hb = (lane >> 4) & 1;
+    const int r4 = (lane & 15) >> 2, q4 = lane & 3, hbit = (lane >> 4) & 1;
     const int key0 = g + 4 * r4;
-    const int v0 = key0 * ROWB + ((2 * hb + (q4 >> 1)) ^ key0) * 16 + 8 * (q4 & 1);
+    const int v0 = key0 * ROWB + ((2 * hbit + (q4 >> 1)) ^ key0) * 16 + 8 * (q4 & 1) + hb;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -511,26 +537,36 @@ __global__ __launch_bounds__(NW * 64, BN == 32 ? 3 : 2 / R) void fwd_bf16_fast(c
       }
   };
 
-  const int ntiles = (kv_hi - kv_lo + BN - 1) / BN;
+  // Step t: the workgroup loads tile t of each half (first key
+  // load_base(t)), and this wave computes on keys kv_w + t BN ..
+  auto load_base = [&](int t) { return t < ntiles ? kv_lo + t * BN : kv_hi; };
   auto wave_sees = [&](int t) {
-    const int kt = kv_lo + t * BN;
+    const int kt = kv_w + t * BN;
     return kt < w_hi && kt + BN > w_lo;
   };
   auto needs_mask = [&](int t) {
-    const int kt = kv_lo + t * BN;
+    const int kt = kv_w + t * BN;
     return kt < i_lo || kt + BN > i_hi;
   };
   // Key tiles inside every row's visible range of the workgroup (the
   // intersection [lo(last row), hi(first row)) of its rows) need no mask for
-  // any wave: they form one run [t_plain0, t_plain1) of the sweep.  The first
-  // tile always takes the general step, which sets the softmax reference.
+  // any wave: steps whose tiles (in both halves) all lie there form one run
+  // [t_plain0, t_plain1) of the sweep.  The first step always takes the
+  // general step, which sets the softmax reference.
   int t_plain0 = 1, t_plain1 = 1;
   {
     int wlo, whi, tmp2;
     row_range(mask, W, qend - 1 + off, nk, wlo, tmp2);
     row_range(mask, W, q0 + off, nk, tmp2, whi);
-    const int first = max(1, (wlo - kv_lo + BN - 1) / BN);
-    const int last = max(0, (whi - kv_lo) / BN);  // tiles [0, last) end at or before whi
+    int first = 1, last = ntiles;
+#pragma unroll
+    for (int hh = 0; hh < HALVES; ++hh) {
+      const int base = kv_lo + hh * ntiles * BN;
+      const int tiles_h = min(ntiles, n_key_tiles - hh * ntiles);  // tiles of this half
+      // tiles [first, last) of the half start at or after wlo and end at or before whi
+      first = max(first, (wlo - base + BN - 1) / BN);
+      last = min(last, min(tiles_h, (whi - base) / BN));
+    }
     if (has_item && last > first) {
       t_plain0 = first;
       t_plain1 = last;
@@ -543,15 +579,16 @@ __global__ __launch_bounds__(NW * 64, BN == 32 ? 3 : 2 / R) void fwd_bf16_fast(c
   auto k_rt = [&](int buf) -> const char * { return buf ? k_lds1 : k_lds0; };
   auto v_rt = [&](int buf) -> const char * { return buf ? v_lds1 : v_lds0; };
   auto general_step = [&](int t) __attribute__((always_inline)) {
-    const int kt = kv_lo + t * BN;
+    const int kt = kv_w + t * BN;
     const int buf = t & 1;
     if (t + 1 < ntiles) {
+      const int kn = load_base(t + 1);
       if (buf) {
-        issue_k(kt + BN, std::integral_constant<int, 0>{});
-        issue_v(kt + BN, std::integral_constant<int, 0>{});
+        issue_k(kn, std::integral_constant<int, 0>{});
+        issue_v(kn, std::integral_constant<int, 0>{});
       } else {
-        issue_k(kt + BN, std::integral_constant<int, 1>{});
-        issue_v(kt + BN, std::integral_constant<int, 1>{});
+        issue_k(kn, std::integral_constant<int, 1>{});
+        issue_v(kn, std::integral_constant<int, 1>{});
       }
     }
     if (wave_sees(t)) {
@@ -599,9 +636,8 @@ __global__ __launch_bounds__(NW * 64, BN == 32 ? 3 : 2 / R) void fwd_bf16_fast(c
   // Plain step: one basic block, scheduled so MFMA and softmax work overlap.
   auto plain_step = [&](auto buf_tag, int t) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value;
-    const int kt = kv_lo + t * BN;
     // the last tile's "next" loads are empty (range starts at kv_hi)
-    const int kn = min(kt + BN, kv_hi);
+    const int kn = load_base(t + 1);
     issue_k(kn, std::integral_constant<int, BUF ^ 1>{});
     issue_v(kn, std::integral_constant<int, BUF ^ 1>{});
     f32x16 sc[R][NB];
@@ -634,8 +670,8 @@ __global__ __launch_bounds__(NW * 64, BN == 32 ? 3 : 2 / R) void fwd_bf16_fast(c
   auto max_sweep = [&]() __attribute__((always_inline)) {
     auto step = [&](auto buf_tag, int t) {
       constexpr int BUF = decltype(buf_tag)::value;
-      const int kt = kv_lo + t * BN;
-      issue_k(min(kt + BN, kv_hi), std::integral_constant<int, BUF ^ 1>{});
+      const int kt = kv_w + t * BN;
+      issue_k(load_base(t + 1), std::integral_constant<int, BUF ^ 1>{});
       if (wave_sees(t)) {
         f32x16 sc[R][NB];
         qk(buf_tag, sc);
@@ -679,7 +715,41 @@ __global__ __launch_bounds__(NW * 64, BN == 32 ? 3 : 2 / R) void fwd_bf16_fast(c
     max_sweep();
   }
 
-  if (wave_active) {
+  if constexpr (SPLIT) {
+    // Merge of the key halves: waves 2 and 3 leave each lane's reference,
+    // share of the row sum and unnormalised outputs in LDS (the V buffers
+    // and a corner of the second K buffer, all free after the last barrier),
+    // lane-major so every access is one 64-lane stride; waves 0 and 1 rescale
+    // both partitions to the larger reference m:
+    //   o = o_a 2^(m_a - m) + o_b 2^(m_b - m),  l likewise
+    // (a half with no visible key for a row has reference -inf and weight 0).
+    float *po = reinterpret_cast<float *>((wave & 1) ? v_lds1 : v_lds0);
+    float *pml = reinterpret_cast<float *>(k_lds1) + (wave & 1) * 128;
+    if (wave >= 2 && wave_active) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) po[(db * 16 + j) * 64 + lane] = o[0][db][j];
+      pml[lane] = m_ref[0];
+      pml[64 + lane] = l_run[0];
+    }
+    __syncthreads();
+    if (wave < 2 && wave_active) {
+      const float ma = m_ref[0], mb = pml[lane];
+      const float m = fmaxf(ma, mb);
+      const float fa = ma == kNegInf ? 0.0f : fast_exp2(ma - m);
+      const float fb = mb == kNegInf ? 0.0f : fast_exp2(mb - m);
+      l_run[0] = l_run[0] * fa + pml[64 + lane] * fb;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[0][db][j] = o[0][db][j] * fa + po[(db * 16 + j) * 64 + lane] * fb;
+      m_ref[0] = m;
+    }
+  }
+
+  // (with key halves only waves 0 and 1 store)
+  if (wave_active && (!SPLIT || wave < 2)) {
     // Output rows go through LDS (the wave's own 32 rows of the K buffers,
     // free once the sweep is over): the accumulator holds 4-column pieces of
     // 32 rows, and read back, consecutive lanes hold consecutive 16-byte
@@ -953,16 +1023,25 @@ constexpr int kManyItems = 3072;
 }  // namespace
 
 int rows_per_workgroup_bf16(int) { return kWavesBf16 * 32; }
+int rows_per_workgroup_bf16_halves(int) { return kWavesBf16 * 32 / 2; }
 int rows_per_workgroup_f32(int) { return 128; }
 
 int launch_bf16(const LaunchArgs &a, int head_dim, void *stream) {
+  if (a.key_halves) {
+    switch (head_dim) {
+      case 64: return launch(fwd_bf16_fast<64, kWavesBf16, 1, 32, true>, a, kWavesBf16 * 64, stream);
+      case 72: return launch(fwd_bf16_fast<72, kWavesBf16, 1, 32, true>, a, kWavesBf16 * 64, stream);
+      case 128: return launch(fwd_bf16_fast<128, kWavesBf16, 1, 32, true>, a, kWavesBf16 * 64, stream);
+      default: return static_cast<int>(hipErrorInvalidValue);
+    }
+  }
   switch (head_dim) {
-    case 64: return launch(fwd_bf16_fast<64, kWavesBf16, 1, 64>, a, kWavesBf16 * 64, stream);
-    case 72: return launch(fwd_bf16_fast<72, kWavesBf16, 1, 64>, a, kWavesBf16 * 64, stream);
+    case 64: return launch(fwd_bf16_fast<64, kWavesBf16, 1, 64, false>, a, kWavesBf16 * 64, stream);
+    case 72: return launch(fwd_bf16_fast<72, kWavesBf16, 1, 64, false>, a, kWavesBf16 * 64, stream);
     case 128:
       return a.total_items >= kManyItems
-                 ? launch(fwd_bf16_fast<128, kWavesBf16, 1, 32>, a, kWavesBf16 * 64, stream)
-                 : launch(fwd_bf16_fast<128, kWavesBf16, 1, 64>, a, kWavesBf16 * 64, stream);
+                 ? launch(fwd_bf16_fast<128, kWavesBf16, 1, 32, false>, a, kWavesBf16 * 64, stream)
+                 : launch(fwd_bf16_fast<128, kWavesBf16, 1, 64, false>, a, kWavesBf16 * 64, stream);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
 }

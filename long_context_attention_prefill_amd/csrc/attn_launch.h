@@ -13,6 +13,14 @@ namespace attn {
 // the same stream; each launch writes a disjoint set of output rows.
 constexpr int kMaxSeqsPerLaunch = 64;
 
+// bf16 launches of at most kKeyHalvesFewItems 128-row items (half the CUs of
+// an MI355X), or of at most kKeyHalvesMaxItems (1.5 per CU) whose longest
+// item has at least 1.5 times the mean key count, take key halves: 64-row
+// items, each half of the keys swept by its own pair of waves, so the launch
+// has twice the workgroups.
+constexpr int64_t kKeyHalvesFewItems = 128;
+constexpr int64_t kKeyHalvesMaxItems = 384;
+
 enum MaskKind : int32_t { kCausal = 0, kFull = 1, kWindow = 2 };
 
 // One launch: a group of sequences with at least one query, sorted by query
@@ -53,6 +61,9 @@ struct LaunchArgs {
   // workgroups, and the last one puts both back to zero.
   int32_t *tickets;
   int32_t ticket_from;
+  // bf16 only: 1 = key halves (bm = 64 rows; two pairs of waves sweep the two
+  // halves of each item's key tiles and merge), for launches of few items
+  int32_t key_halves;
 };
 
 // Decode: one query (the newest token) per sequence against its key/value
@@ -113,6 +124,7 @@ constexpr uint64_t kDecodeScratchBytes = 16ull << 20;
 int decode_scratch(void *stream, void **ptr);
 // Query rows per workgroup of each family (the planner tiles with it).
 int rows_per_workgroup_bf16(int head_dim);
+int rows_per_workgroup_bf16_halves(int head_dim);  // with key halves
 int rows_per_workgroup_f32(int head_dim);
 
 // For a causal bf16 launch with many more items than workgroup slots: point

@@ -14,6 +14,7 @@ int launch_bf16(const LaunchArgs &, int, void *) { return 1; }
 int launch_f32(const LaunchArgs &, int, void *) { return 1; }
 int launch_decode_bf16(const DecodeArgs &, int, void *) { return 1; }
 int rows_per_workgroup_bf16(int) { return 128; }
+int rows_per_workgroup_bf16_halves(int) { return 64; }
 int rows_per_workgroup_f32(int) { return 128; }
 int decode_scratch(void *, void **ptr) {
   *ptr = nullptr;
