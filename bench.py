@@ -454,6 +454,18 @@ def cpu_baseline():
     }
 
 
+def copy_calibration():
+    """Three plain device copies of known traffic (256 MiB read + 256 MiB
+    written each), against which HBM counters are scaled."""
+    import torch
+
+    src = torch.ones(128 << 20, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -466,6 +478,9 @@ def main():
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the N = 2048..10240 sweep (16/2 heads, causal) and the fp32 line")
+    ap.add_argument("--workload", choices=["2", "4", "5a", "5b"],
+                    help="time only this one of the other workloads, sampled as in the full run, "
+                         "and print its summary (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -480,6 +495,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     lcap.load_library()
+
+    if args.workload:
+        w = W.WORKLOADS[args.workload]
+        hst, dv = device_inputs(w)
+        res = summarize(w, *sample_calls(w, dv, hst[3]))
+        if args.copy_calibration:
+            copy_calibration()
+        print(json.dumps({"workload_only": res}), flush=True)
+        return
 
     w10 = W.WORKLOADS["3"]
     host10, dev10 = device_inputs(w10)
@@ -561,12 +585,7 @@ def main():
         torch.cuda.empty_cache()
 
     if args.copy_calibration:
-        # known traffic: 256 MiB read + 256 MiB written per copy kernel
-        src = torch.ones(128 << 20, dtype=torch.bfloat16, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+        copy_calibration()
 
     traffic = read_traffic()
     counters = read_counters()

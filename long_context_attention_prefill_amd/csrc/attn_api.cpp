@@ -174,6 +174,12 @@ int run(const void *q, const void *k, const void *v, void *out, float *lse,
     }
     if (items > INT32_MAX) return ATTN_EUNSUPPORTED;
     a.total_items = static_cast<int32_t>(items);
+    // window launches whose windows span at most two query tiles: whole runs
+    // of 16 query tiles (two per XCD) in the XCD-blocked order, so a window's
+    // keys and values reach one XCD's L2 once for every head
+    a.xcd_tiles = mask_kind == ATTN_WINDOW && window <= 2 * bm_l
+                      ? static_cast<int32_t>(((items / n_q_heads) / 16) * 16)
+                      : 0;
     // causal item order: levels [seq_tiles[k], seq_tiles[k-1]) of the k longest
     // sequences follow each other, longest level first
     int64_t start = 0;

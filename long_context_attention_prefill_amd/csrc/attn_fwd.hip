@@ -81,15 +81,31 @@ __device__ __forceinline__ Item decode_item(const LaunchArgs &a, int r) {
     it.seq = rem / a.hq;
     slot = rem - it.seq * a.hq;
   } else {
+    // Full and window launches.  Workgroup r runs on XCD r mod 8; with
+    // a.xcd_tiles set (windows of at most two query tiles) the first
+    // a.xcd_tiles query tiles (in sequence order) go to the XCDs in runs of
+    // two consecutive tiles, all heads of a run back to back on one XCD, so
+    // the keys and values of a window reach that XCD's L2 once for all its
+    // heads (in the plain order each XCD holds a block of query heads for
+    // every tile, and each key/value head is fetched by every XCD holding
+    // one of its query heads).  Tiles past them keep the plain order.
+    int g = 0;  // tile index over the launch's sequences
+    if (r < a.xcd_tiles * a.hq) {
+      const int x = r & 7, q = r >> 3;
+      const int run = q / (2 * a.hq), in_run = q - run * 2 * a.hq;
+      g = run * 16 + 2 * x + in_run / a.hq;
+      slot = in_run - (in_run / a.hq) * a.hq;
+    } else {
+      g = r / a.hq;
+      slot = r - g * a.hq;
+    }
     for (int b = 0; b < a.n_seqs; ++b) {
-      const int cnt = a.seq_tiles[b] * a.hq;
-      if (r < cnt) {
+      if (g < a.seq_tiles[b]) {
         it.seq = b;
-        it.tile = r / a.hq;
-        slot = r - it.tile * a.hq;
+        it.tile = g;
         break;
       }
-      r -= cnt;
+      g -= a.seq_tiles[b];
     }
   }
   it.head = (a.hq % 8 == 0) ? (slot & 7) * (a.hq >> 3) + (slot >> 3) : slot;

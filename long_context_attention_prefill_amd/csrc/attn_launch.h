@@ -64,6 +64,9 @@ struct LaunchArgs {
   // bf16 only: 1 = key halves (bm = 64 rows; two pairs of waves sweep the two
   // halves of each item's key tiles and merge), for launches of few items
   int32_t key_halves;
+  // full and window masks: the first xcd_tiles query tiles (a multiple of 16)
+  // run XCD by XCD in runs of two tiles (see decode_item); 0 = plain order
+  int32_t xcd_tiles;
 };
 
 // Decode: one query (the newest token) per sequence against its key/value
