@@ -712,18 +712,23 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
     if (pass == 1) break;
     // A row whose sum or output overflowed: the workgroup redoes its rows
     // with the exact row maxima as references.
+    // x * 0 is 0 for finite x and NaN for an infinity or a NaN, so one sum
+    // of such products flags every non-finite value of a row; a test per
+    // element (short-circuit ||) compiles to a branch per accumulator entry,
+    // microseconds per workgroup.  Entry j of block db holds columns
+    // 32 db + 8 (j >> 2) .. +7 of O^T across both lane halves, all real or
+    // all padding, since D is a multiple of 8.
     bool bad = false;
     if (wave_active) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const float l_tot = l_run[r] + xor32(l_run[r]);
-        bad = bad || (row_ok[r] && !__builtin_isfinite(l_tot));
+        float probe = (l_run[r] + xor32(l_run[r])) * 0.0f;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int j = 0; j < 16; ++j)
-            bad = bad || (row_ok[r] && 32 * db + 8 * (j >> 2) + 4 * g + (j & 3) < D &&
-                          !__builtin_isfinite(o[r][db][j]));
+            if (32 * db + 8 * (j >> 2) < D) probe = __builtin_fmaf(o[r][db][j], 0.0f, probe);
+        bad = bad || (row_ok[r] && !__builtin_isfinite(probe));
       }
     }
     if (!__syncthreads_or(bad)) break;
