@@ -56,6 +56,16 @@ struct Item {
   int head;
 };
 
+// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time
+// (for builtins whose operands must be constants).
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // Workgroup r -> (sequence, query tile, query head), heaviest work first.
 // Causal: tile m costs ~(m+1) key tiles in every sequence, so items are
 // ordered by m descending across the batch, the sequences holding a level in
@@ -184,13 +194,14 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
   constexpr bool XOR = D == 128;
   constexpr int ROWB = XOR ? D * 2 : L::ROWB;  // bytes per key row in LDS
   constexpr int KBUF = HALVES * BN * ROWB;  // bytes per K (or V) LDS tile (both halves)
-  // A tile is NLOADS wave-wide direct loads (64 lanes x 16 bytes); each wave
-  // issues NL of them, and a wave whose last load falls past the tile sends
-  // it, all lanes out of range, into a 1 KB spill slot after the tile, so
-  // the issue code has no branches.
+  // A tile is NLOADS wave-wide direct loads (64 lanes x 16 bytes); wave w
+  // issues NL of them, into the consecutive 1 KB slots NL w .. NL w + NL - 1,
+  // and slots past the tile (when NW does not divide NLOADS) take loads with
+  // every lane out of range that nothing reads, so the issue code has no
+  // branches.
   constexpr int NLOADS = KBUF / 1024;
   constexpr int NL = (NLOADS + NW - 1) / NW;
-  constexpr int BUF_BYTES = KBUF + (NL * NW > NLOADS ? 1024 : 0);  // one LDS buffer
+  constexpr int BUF_BYTES = NL * NW * 1024;  // one LDS buffer
   static_assert(NLOADS * 1024 == KBUF, "a tile is a whole number of wave-wide loads");
 
   // One array per buffer half: the compiler can then tell that a direct
@@ -284,7 +295,8 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
                                                    : (bf16x8)((__bf16)0.0f);
   }
 
-  // Direct loads: wave-wide load j fills LDS slots 64j .. 64j+63 of a tile.
+  // Direct loads: wave-wide load j fills LDS slots 64j .. 64j+63 of a tile;
+  // wave w's i-th load is load j = NL w + i.
   // Padded layout: slot p is row p / SLOTS, chunk p % SLOTS (chunks >= CH are
   // padding).  XOR layout: load j fills keys 4j .. 4j+3, lane l writing key
   // 4j + (l >> 4), slot l & 15, which holds chunk (l & 15) ^ (key & 15).
@@ -296,19 +308,29 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
   const int ntiles = SPLIT ? (n_key_tiles + 1) / 2 : n_key_tiles;  // steps of a sweep
   const int kv_w = kv_lo + half * ntiles * BN;  // first key of this wave's half
   const uint32_t b_shift = SPLIT ? (uint32_t)((ntiles - 1) * BN * rowbytes) : 0u;
+  // Load i of a wave goes out with immediate offset (i mod 4) KB, which the
+  // hardware adds to the LDS address (M0) and to the memory offset, range
+  // check included; so four loads share one M0.  The memory side takes it
+  // back through the lane offset, kept non-negative by a descriptor whose
+  // base sits kLoadBias bytes before the tile (and whose range is that much
+  // longer): lane offset = kLoadBias + (offset in the tile) - immediate.
+  constexpr uint32_t kLoadBias = 4096;
   uint32_t ld_off[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
+    const int j = NL * wave + i;
+    const uint32_t bias = kLoadBias - 1024u * (uint32_t)(i & 3);
     if constexpr (XOR) {
-      const int key = 4 * (wave + NW * i) + (lane >> 4);
+      const int key = 4 * j + (lane >> 4);
       ld_off[i] = key < HALVES * BN ? (uint32_t)(key * rowbytes + ((lane & 15) ^ (key & 15)) * 16) +
-                                          (key >= BN ? b_shift : 0u)
+                                          (key >= BN ? b_shift : 0u) + bias
                                     : kOutOfRange;
     } else {
-      const int p = (wave + NW * i) * 64 + lane;
+      const int p = j * 64 + lane;
       const int rr = p / L::SLOTS, cs = p % L::SLOTS;
-      ld_off[i] = cs < CH && rr < HALVES * BN ? (uint32_t)(rr * rowbytes + cs * 16) + (rr >= BN ? b_shift : 0u)
-                                              : kOutOfRange;
+      ld_off[i] = cs < CH && rr < HALVES * BN
+                      ? (uint32_t)(rr * rowbytes + cs * 16) + (rr >= BN ? b_shift : 0u) + bias
+                      : kOutOfRange;
     }
   }
   const char *kseq = reinterpret_cast<const char *>(a.k) + ((size_t)s0k * a.kv_stride + (size_t)hk * D) * 2;
@@ -320,14 +342,16 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
   // the (unused) buffer fills with zeros, so a step needs no branch.
   auto issue = [&](const char *seq, char *lds, int kt) {
     const int nrows = SPLIT ? kv_hi - kt : min(kv_hi - kt, BN);
-    const int rec = max(0, (nrows - 1) * rowbytes + D * 2);  // later rows read as zeros
+    // later rows read as zeros
+    const int rec = max(0, (nrows - 1) * rowbytes + D * 2) + (int)kLoadBias;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(seq + (size_t)kt * rowbytes), (short)0, rec, kBufferWord3);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int j = min(wave + NW * i, NLOADS);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(lds + j * 1024), 16, ld_off[i], 0, 0, 0);
-    }
+        reinterpret_cast<char *>(reinterpret_cast<uintptr_t>(seq) + (size_t)kt * rowbytes - kLoadBias), (short)0,
+        rec, kBufferWord3);
+    static_for<0, NL>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(lds + (NL * wave + (i & ~3)) * 1024), 16,
+                                               ld_off[i], 0, 1024 * (i & 3), 0);
+    });
   };
   auto issue_k = [&](int kt, auto buf_tag) { issue(kseq, k_buf(buf_tag), kt); };
   auto issue_v = [&](int kt, auto buf_tag) { issue(vseq, v_buf(buf_tag), kt); };
