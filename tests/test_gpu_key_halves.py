@@ -138,3 +138,28 @@ def test_halves_probe_count(mask):
     q, k, v = W.probe_count_inputs(cu, hq, hkv, d)
     got = G.run_hip(q, k, v, cu, mask, 1.0 / math.sqrt(d), "bf16")
     probes.check_count_output(got, cu, mask, d)
+
+
+@pytest.mark.parametrize("sign", [1, -1])
+@pytest.mark.parametrize("mask", ["causal", "full", ("window", 256)], ids=str)
+@pytest.mark.parametrize("d", [64, 72, 128])
+def test_whole_rows_probe_index(d, mask, sign):
+    """The same exact probes on a launch of many items (whole 128-row tiles,
+    64-key steps at every head dim): first or last visible key and KV head at
+    every row, with the probe's overflow and re-sweep in every workgroup."""
+    cu, hq, hkv = np.array([0, 3000, 3001, 4100]), 16, 16
+    assert not takes_halves(cu, cu, hq, mask)
+    q, k, v = W.probe_index_inputs(cu, hq, hkv, d, sign)
+    got = G.run_hip(q, k, v, cu, mask, 1.0 / math.sqrt(d), "bf16")
+    probes.check_index_output(got, cu, mask, hq, hkv, sign)
+
+
+@pytest.mark.parametrize("mask", ["causal", "full", ("window", 300)], ids=str)
+@pytest.mark.parametrize("d", [64, 72])
+def test_whole_rows_probe_count(d, mask):
+    """Every row of a launch of many items: exact count of visible keys."""
+    cu, hq, hkv = np.array([0, 3000, 3001, 4100]), 16, 2
+    assert not takes_halves(cu, cu, hq, mask)
+    q, k, v = W.probe_count_inputs(cu, hq, hkv, d)
+    got = G.run_hip(q, k, v, cu, mask, 1.0 / math.sqrt(d), "bf16")
+    probes.check_count_output(got, cu, mask, d)
