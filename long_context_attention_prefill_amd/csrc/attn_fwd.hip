@@ -172,7 +172,7 @@ __device__ __forceinline__ void row_range(int mask, int W, int i, int n, int &lo
 // references, sums and unnormalised outputs to waves 0 and 1 through LDS,
 // which fold them in (the merge of two softmax partitions) and store.  Twice
 // the workgroups of the plain split by rows, each half as long.
-template <int D, int NW, int R, int BN, bool SPLIT>
+template <int D, int NW, int R, int BN, bool SPLIT, bool SHIFT>
 __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_bf16_fast(const LaunchArgs a) {
   // The host pass only needs this kernel's signature for its launch stub;
   // the body (gfx950-only builtins) is compiled for the device alone.
@@ -192,6 +192,15 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
   // head_dim 128: unpadded 256-byte key rows whose 16-byte chunk c sits at
   // slot c ^ (key mod 16) (the XOR layout); 64 and 72: the padded layout
   constexpr bool XOR = D == 128;
+  // SHIFT (scales |c| <= kPrescaleMaxC): the query fragments hold c q rounded
+  // to bf16, so S^T leaves the MFMAs in exp2 units, and plain steps start
+  // S^T from -m (one register block per sub-block, fixed for the sweep)
+  // instead of subtracting m per score: one VALU op fewer per score.  The
+  // extra rounding perturbs each score by about |c| 2^-9 |q . k| (relative
+  // 2^-9 per query element), which is why larger scales keep exact queries
+  // and the per-score FMA; so does the 32-key instance at three workgroups
+  // per CU, which has no registers to spare.
+  static_assert(!SHIFT || !(BN == 32 && !SPLIT), "no shifted start on the 32-key, three-workgroup instance");
   constexpr int ROWB = XOR ? D * 2 : L::ROWB;  // bytes per key row in LDS
   constexpr int KBUF = HALVES * BN * ROWB;  // bytes per K (or V) LDS tile (both halves)
   // A tile is NLOADS wave-wide direct loads (64 lanes x 16 bytes); wave w
@@ -283,16 +292,22 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
   }
 
   // Q fragments (B operand of S^T = K Q^T): lane (l32, g) of sub-block r
-  // holds q[row[r]][16*kk + 8*g .. +7].
+  // holds q[row[r]][16*kk + 8*g .. +7] (with SHIFT scaled by c and rounded to
+  // bf16, so S^T comes out of the MFMAs in exp2 units).
   bf16x8 qf[R][KST];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const __bf16 *qrow = reinterpret_cast<const __bf16 *>(a.q) +
                          (size_t)(s0q + (row_ok[r] ? row[r] : 0)) * a.q_stride + (size_t)h * D;
 #pragma unroll
-    for (int kk = 0; kk < KST; ++kk)
+    for (int kk = 0; kk < KST; ++kk) {
       qf[r][kk] = row_ok[r] && 16 * kk + 8 * g < D ? *reinterpret_cast<const bf16x8 *>(qrow + 16 * kk + 8 * g)
                                                    : (bf16x8)((__bf16)0.0f);
+      if constexpr (SHIFT) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[r][kk][e] = (__bf16)((float)qf[r][kk][e] * c);
+      }
+    }
   }
 
   // Direct loads: wave-wide load j fills LDS slots 64j .. 64j+63 of a tile;
@@ -433,17 +448,22 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
     const int key = kt + nb * 32 + 16 * (j >> 3) + 2 * ((j >> 2) & 1) + 4 * (j & 3) + g;
     return key >= lo_r[r] && key < hi_r[r];
   };
-  // a score that becomes -inf once multiplied by c
-  const float s_void = neg ? __builtin_huge_valf() : kNegInf;
+  // a masked score: -inf in exp2 units (SHIFT), else a score that becomes
+  // -inf once multiplied by c
+  const float s_void = SHIFT || !neg ? kNegInf : __builtin_huge_valf();
 
   // S^T = K Q^T for the 64 keys held in K buffer KB, every sub-block; each K
   // fragment feeds the R sub-blocks' MFMAs in a row.
-  auto qk = [&](auto kbuf_tag, f32x16 (&sc)[R][NB]) {
+  // With SHIFT the accumulation starts from -m (neg_ref) instead of 0, so the
+  // scores leave the MFMAs as c s - m, ready for exp2.
+  f32x16 neg_ref[R];
+  auto qk = [&](auto kbuf_tag, f32x16 (&sc)[R][NB], auto shift_tag) {
+    constexpr bool SHIFTED = decltype(shift_tag)::value;
     const char *kb = k_buf(kbuf_tag);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) sc[r][nb] = (f32x16)(0.0f);
+      for (int r = 0; r < R; ++r) sc[r][nb] = SHIFTED ? neg_ref[r] : (f32x16)(0.0f);
 #pragma unroll
       for (int kk = 0; kk < KST; ++kk) {
         const bf16x8 kf = kfrag(kb, nb, kk);
@@ -526,7 +546,7 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
   // Row maximum of c*s over the tile for sub-block r, both lane halves combined.
   auto row_max = [&](const f32x16 (&scr)[NB]) {
     float mx = kNegInf;
-    if (neg) {
+    if (!SHIFT && neg) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -537,14 +557,16 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = fmaxf(mx, scr[nb][j]);
     }
-    const float mt = mx * cabs;
+    const float mt = SHIFT ? mx : mx * cabs;
     return fmaxf(mt, xor32(mt));
   };
   // P = exp2(c*s - m) as bf16 B operands of O^T = V^T P^T, and the row sum
-  // of those same bf16 values.  k step ks covers keys 16ks .. 16ks+15, held
-  // in accumulator entries 8*(ks&1) .. +7 of block ks>>1; entry e of lane
-  // half g is key 16ks + g + 4(e & 3) + 2(e >> 2).
-  auto softmax = [&](f32x16 (&sc)[R][NB], bf16x8 (&pf)[R][BN / 16]) {
+  // of those same bf16 values (SHIFTED: the scores hold c*s - m already).
+  // k step ks covers keys 16ks .. 16ks+15, held in accumulator entries
+  // 8*(ks&1) .. +7 of block ks>>1; entry e of lane half g is key
+  // 16ks + g + 4(e & 3) + 2(e >> 2).
+  auto softmax = [&](f32x16 (&sc)[R][NB], bf16x8 (&pf)[R][BN / 16], auto shift_tag) {
+    constexpr bool SHIFTED = decltype(shift_tag)::value;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int ks = 0; ks < BN / 16; ++ks)
@@ -553,8 +575,10 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
         // a row with no visible key yet has every score at -inf here
         const float neg_m = m_ref[r] == kNegInf ? 0.0f : -m_ref[r];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pf[r][ks][e] = (__bf16)fast_exp2(__builtin_fmaf(sc[r][ks >> 1][8 * (ks & 1) + e], c, neg_m));
+        for (int e = 0; e < 8; ++e) {
+          const float x = sc[r][ks >> 1][8 * (ks & 1) + e];
+          pf[r][ks][e] = (__bf16)fast_exp2(SHIFTED ? x : SHIFT ? x + neg_m : __builtin_fmaf(x, c, neg_m));
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bf16x2 pr = {pf[r][ks][2 * e], pf[r][ks][2 * e + 1]};
@@ -656,7 +680,7 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
           m_ref[r] = m_ref[r] == kNegInf ? mt : m_ref[r];
         }
       bf16x8 pf[R][BN / 16];
-      softmax(sc, pf);
+      softmax(sc, pf, std::false_type{});
       {
         const char *vb = v_rt(buf);
 #pragma unroll
@@ -682,8 +706,8 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
     issue_v(kn, std::integral_constant<int, BUF ^ 1>{});
     f32x16 sc[R][NB];
     bf16x8 pf[R][BN / 16];
-    qk(buf_tag, sc);
-    softmax(sc, pf);
+    qk(buf_tag, sc, std::integral_constant<bool, SHIFT>{});
+    softmax(sc, pf, std::integral_constant<bool, SHIFT>{});
     pv(buf_tag, pf);
     plain_tile_schedule();
     __builtin_amdgcn_s_waitcnt(0);
@@ -698,6 +722,10 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
     __syncthreads();
     int t = 0;
     for (; t < t_plain0 && t < ntiles; ++t) general_step(t);
+    if constexpr (SHIFT) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) neg_ref[r] = (f32x16)(m_ref[r] == kNegInf ? 0.0f : -m_ref[r]);
+    }
     if (t < t_plain1 && (t & 1)) plain_step(std::integral_constant<int, 1>{}, t++);
     for (; t + 1 < t_plain1; t += 2) {
       plain_step(std::integral_constant<int, 0>{}, t);
@@ -714,7 +742,7 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
       issue_k(load_base(t + 1), std::integral_constant<int, BUF ^ 1>{});
       if (wave_sees(t)) {
         f32x16 sc[R][NB];
-        qk(buf_tag, sc);
+        qk(buf_tag, sc, std::false_type{});
         if (needs_mask(t)) apply_mask(sc, kt);
 #pragma unroll
         for (int r = 0; r < R; ++r) m_ref[r] = fmaxf(m_ref[r], row_max(sc[r]));
@@ -1065,6 +1093,15 @@ constexpr int kWavesBf16 = 4;
 // longer items faster (10k causal +2 %, 2k causal +2 % with 32-key tiles)
 constexpr int kManyItems = 3072;
 
+// The prescaled-query instance of a kernel for scales up to kPrescaleMaxC,
+// the exact-query one above.
+template <int D, int R, int BN, bool SPLIT>
+int launch_sh(const LaunchArgs &a, void *stream) {
+  return (a.c <= kPrescaleMaxC && a.c >= -kPrescaleMaxC)
+             ? launch(fwd_bf16_fast<D, kWavesBf16, R, BN, SPLIT, true>, a, kWavesBf16 * 64, stream)
+             : launch(fwd_bf16_fast<D, kWavesBf16, R, BN, SPLIT, false>, a, kWavesBf16 * 64, stream);
+}
+
 }  // namespace
 
 int rows_per_workgroup_bf16(int) { return kWavesBf16 * 32; }
@@ -1074,19 +1111,19 @@ int rows_per_workgroup_f32(int) { return 128; }
 int launch_bf16(const LaunchArgs &a, int head_dim, void *stream) {
   if (a.key_halves) {
     switch (head_dim) {
-      case 64: return launch(fwd_bf16_fast<64, kWavesBf16, 1, 32, true>, a, kWavesBf16 * 64, stream);
-      case 72: return launch(fwd_bf16_fast<72, kWavesBf16, 1, 32, true>, a, kWavesBf16 * 64, stream);
-      case 128: return launch(fwd_bf16_fast<128, kWavesBf16, 1, 32, true>, a, kWavesBf16 * 64, stream);
+      case 64: return launch_sh<64, 1, 32, true>(a, stream);
+      case 72: return launch_sh<72, 1, 32, true>(a, stream);
+      case 128: return launch_sh<128, 1, 32, true>(a, stream);
       default: return static_cast<int>(hipErrorInvalidValue);
     }
   }
   switch (head_dim) {
-    case 64: return launch(fwd_bf16_fast<64, kWavesBf16, 1, 64, false>, a, kWavesBf16 * 64, stream);
-    case 72: return launch(fwd_bf16_fast<72, kWavesBf16, 1, 64, false>, a, kWavesBf16 * 64, stream);
+    case 64: return launch_sh<64, 1, 64, false>(a, stream);
+    case 72: return launch_sh<72, 1, 64, false>(a, stream);
     case 128:
       return a.total_items >= kManyItems
-                 ? launch(fwd_bf16_fast<128, kWavesBf16, 1, 32, false>, a, kWavesBf16 * 64, stream)
-                 : launch(fwd_bf16_fast<128, kWavesBf16, 1, 64, false>, a, kWavesBf16 * 64, stream);
+                 ? launch(fwd_bf16_fast<128, kWavesBf16, 1, 32, false, false>, a, kWavesBf16 * 64, stream)
+                 : launch_sh<128, 1, 64, false>(a, stream);
     default: return static_cast<int>(hipErrorInvalidValue);
   }
 }

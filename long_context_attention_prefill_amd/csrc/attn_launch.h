@@ -21,6 +21,13 @@ constexpr int kMaxSeqsPerLaunch = 64;
 constexpr int64_t kKeyHalvesFewItems = 128;
 constexpr int64_t kKeyHalvesMaxItems = 384;
 
+// bf16 launches whose exp2-unit scale c = scale * log2(e) has |c| at most
+// this take the query pre-multiplied by c and rounded to bf16 (scores leave
+// the MFMAs in exp2 units; each moves by about |c| 2^-9 |q . k|): every usual
+// 1/sqrt(d) scale (|c| = 0.18 at d 64, 0.13 at d 128).  Larger scales, whose
+// sharper softmax would magnify that rounding, keep the exact query.
+constexpr float kPrescaleMaxC = 0.25f;
+
 enum MaskKind : int32_t { kCausal = 0, kFull = 1, kWindow = 2 };
 
 // One launch: a group of sequences with at least one query, sorted by query

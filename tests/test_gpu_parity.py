@@ -75,7 +75,9 @@ def test_fuzz_f32(orc, seed):
     assert G.max_err(got, want) <= G.TOL["f32"], (c["cu"].tolist(), c["mask"], c["d"])
 
 
-@pytest.mark.parametrize("scale", [0.0, -0.3, 2.5])
+# bf16: 0, -0.1 and 0.15 run the prescaled-query kernels (|scale log2 e| <=
+# 0.25), -0.3 and 2.5 the exact-query ones
+@pytest.mark.parametrize("scale", [0.0, -0.1, 0.15, -0.3, 2.5])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_unusual_scales(orc, dtype, scale):
     cu = [0, 200, 450]
