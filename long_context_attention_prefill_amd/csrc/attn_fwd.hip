@@ -1086,11 +1086,14 @@ int launch(K kernel, const LaunchArgs &a, int threads, void *stream) {
 }
 
 constexpr int kWavesBf16 = 4;
-// head_dim 128 launches of at least this many items (12 rounds of 256 CUs'
-// workgroups) take 32-key tiles at three workgroups per CU: the third
-// workgroup hides more of each item's fixed costs (packed window-256 batch
-// -11 %, packed causal batch -2 %) while 64-key tiles run a launch of fewer,
-// longer items faster (10k causal +2 %, 2k causal +2 % with 32-key tiles)
+// head_dim 128 full and window launches of at least this many items (12
+// rounds of 256 CUs' workgroups) take 32-key tiles at three workgroups per
+// CU: the third workgroup hides more of each item's fixed costs (packed
+// window-256 batch -11 %).  Causal launches keep 64-key tiles at two
+// workgroups per CU, whose plain steps start S^T from -m (the 32-key
+// instance has no registers for that): packed causal batch -2 % against
+// 32-key tiles, which were 2 % faster than 64-key tiles with the per-score
+// FMA.
 constexpr int kManyItems = 3072;
 
 // The prescaled-query instance of a kernel for scales up to kPrescaleMaxC,
@@ -1121,7 +1124,7 @@ int launch_bf16(const LaunchArgs &a, int head_dim, void *stream) {
     case 64: return launch_sh<64, 1, 64, false>(a, stream);
     case 72: return launch_sh<72, 1, 64, false>(a, stream);
     case 128:
-      return a.total_items >= kManyItems
+      return a.total_items >= kManyItems && a.mask_kind != kCausal
                  ? launch(fwd_bf16_fast<128, kWavesBf16, 1, 32, false, false>, a, kWavesBf16 * 64, stream)
                  : launch_sh<128, 1, 64, false>(a, stream);
     default: return static_cast<int>(hipErrorInvalidValue);

@@ -1,10 +1,10 @@
-"""head_dim-128 launches of many items (>= 3072 workgroups), which run
-32-key tiles at three workgroups per CU: element-wise against the fp64
-oracle where it finishes in seconds (window and full masks over packed
-batches, every row), and for causal at that size through the exact probes
-at every row (mask, first and last visible key, KV head map) plus sampled
-oracle rows.  Ragged lengths put partial tiles and empty sequences in the
-batch."""
+"""head_dim-128 launches of many items (>= 3072 workgroups): window and
+full masks run 32-key tiles at three workgroups per CU, causal masks 64-key
+tiles with work tickets.  Element-wise against the fp64 oracle where it
+finishes in seconds (window and full masks over packed batches, every row),
+and for causal at that size through the exact probes at every row (mask,
+first and last visible key, KV head map) plus sampled oracle rows.  Ragged
+lengths put partial tiles and empty sequences in the batch."""
 import math
 
 import numpy as np
