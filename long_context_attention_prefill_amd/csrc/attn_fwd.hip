@@ -1096,11 +1096,11 @@ constexpr int kWavesBf16 = 4;
 // FMA.
 constexpr int kManyItems = 3072;
 
-// The prescaled-query instance of a kernel for scales up to kPrescaleMaxC,
-// the exact-query one above.
+// The prescaled-query instance of a kernel for scales up to kPrescaleMaxC
+// when no log-sum-exp is returned, the exact-query one otherwise.
 template <int D, int R, int BN, bool SPLIT>
 int launch_sh(const LaunchArgs &a, void *stream) {
-  return (a.c <= kPrescaleMaxC && a.c >= -kPrescaleMaxC)
+  return (a.lse == nullptr && a.c <= kPrescaleMaxC && a.c >= -kPrescaleMaxC)
              ? launch(fwd_bf16_fast<D, kWavesBf16, R, BN, SPLIT, true>, a, kWavesBf16 * 64, stream)
              : launch(fwd_bf16_fast<D, kWavesBf16, R, BN, SPLIT, false>, a, kWavesBf16 * 64, stream);
 }

@@ -25,7 +25,9 @@ constexpr int64_t kKeyHalvesMaxItems = 384;
 // this take the query pre-multiplied by c and rounded to bf16 (scores leave
 // the MFMAs in exp2 units; each moves by about |c| 2^-9 |q . k|): every usual
 // 1/sqrt(d) scale (|c| = 0.18 at d 64, 0.13 at d 128).  Larger scales, whose
-// sharper softmax would magnify that rounding, keep the exact query.
+// sharper softmax would magnify that rounding, keep the exact query, and so
+// do launches that return the log-sum-exp (for a row with one visible key it
+// is that key's score, where the rounding would show undamped).
 constexpr float kPrescaleMaxC = 0.25f;
 
 enum MaskKind : int32_t { kCausal = 0, kFull = 1, kWindow = 2 };
