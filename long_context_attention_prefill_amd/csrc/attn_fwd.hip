@@ -452,8 +452,10 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
   // -inf once multiplied by c
   const float s_void = SHIFT || !neg ? kNegInf : __builtin_huge_valf();
 
-  // S^T = K Q^T for the 64 keys held in K buffer KB, every sub-block; each K
-  // fragment feeds the R sub-blocks' MFMAs in a row.
+  // S^T = K Q^T for the keys held in K buffer KB, every sub-block; each K
+  // fragment feeds the R sub-blocks' MFMAs in a row.  The k steps are the
+  // outer loop, so the NB 32-key blocks' accumulation chains interleave and
+  // no MFMA issues right behind the one it accumulates onto.
   // With SHIFT the accumulation starts from -m (neg_ref) instead of 0, so the
   // scores leave the MFMAs as c s - m, ready for exp2.
   f32x16 neg_ref[R];
@@ -461,26 +463,23 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
     constexpr bool SHIFTED = decltype(shift_tag)::value;
     const char *kb = k_buf(kbuf_tag);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int r = 0; r < R; ++r) sc[r][nb] = SHIFTED ? neg_ref[r] : (f32x16)(0.0f);
 #pragma unroll
-      for (int kk = 0; kk < KST; ++kk) {
+    for (int kk = 0; kk < KST; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
         const bf16x8 kf = kfrag(kb, nb, kk);
 #pragma unroll
         for (int r = 0; r < R; ++r)
           sc[r][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[r][kk], sc[r][nb], 0, 0, 0);
       }
-    }
   };
-  // Schedule of a plain tile (one basic block): the MFMAs of the second
-  // 32-key block of S^T run under the softmax of the first, and the PV MFMAs
-  // of the first two k steps under the softmax of the second, with a few LDS
-  // reads kept ahead of their MFMAs and the next tile's loads one per MFMA
-  // of the first block (any left over follow: issued in a burst, eight
-  // waves' loads back up the CU's load pipe and stall the MFMA issue; one
-  // per MFMA measured 0.7 % faster at 10k and 3-7 % at 1-2k tokens) (mask:
-  // 2 VALU, 8 MFMA, 0x20 VMEM read, 0x100 DS read).
+  // Schedule of a plain tile (one basic block; sched_group_barrier masks:
+  // 0x2 VALU, 0x8 MFMA, 0x20 VMEM read, 0x100 DS read, 0x400 transcendental
+  // -- the VALU mask does not cover v_exp_f32, which only the 0x400 groups
+  // place).
   auto plain_tile_schedule = [&]() {
     if constexpr (NB == 1) {
       // 32-key tiles: S^T with the next tile's loads, the softmax of the
@@ -508,31 +507,34 @@ __global__ __launch_bounds__(NW * 64, BN == 32 && !SPLIT ? 3 : 2 / R) void fwd_b
       }
       return;
     }
-    constexpr int SOFT = 3 * (BN / 2) / KST;  // softmax VALU ops per QK MFMA
-    constexpr int PV_HALF = DB * (BN / 32);   // PV k-step pairs' fragments
+    // 64-key tiles: three coarse phases.  Two waves of different workgroups
+    // share each SIMD, and the matrix pipe stays busiest when each wave
+    // alternates long MFMA runs with long VALU runs, so that one wave's
+    // softmax burst runs under the other wave's MFMAs: all of S^T (the two
+    // blocks' chains interleaved) with the K fragment reads four ahead and
+    // the next tile's loads one per two MFMAs; then the whole tile's
+    // softmax as one burst (exp2, conversion, row sums); then PV with its V
+    // fragments read one MFMA ahead.  Measured on the 10k causal launch
+    // against the earlier order (block 1's S^T under block 0's softmax, PV
+    // steps under block 1's softmax): 1.9 % faster; spreading the exp2 two
+    // per MFMA instead was 4 % slower, and putting the loads inside the
+    // softmax burst 3 % slower.
+    constexpr int QK_MFMA = NB * KST * R;
+    constexpr int PV_MFMA = (BN / 16) * DB * R;
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < KST; ++i) {  // S^T block 0, with the next tile's loads
-      __builtin_amdgcn_sched_group_barrier(0x008, R, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    for (int i = 0; i < QK_MFMA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i % 2 == 1 && i / 2 < 2 * NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x400, (BN / 2) * R, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, BN * R, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int i = 0; i < KST * R; ++i) {  // S^T block 1 under softmax of block 0
+    for (int i = 0; i < PV_MFMA; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, SOFT, 0);
-      if (i % R == R - 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < PV_HALF * R; ++i) {  // PV of k steps 0-1 under softmax of block 1
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2 * KST * SOFT / PV_HALF, 0);
-      if (i % R == R - 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < PV_HALF * R; ++i) {  // PV of k steps 2-3
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i % R == R - 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
   auto apply_mask = [&](f32x16 (&sc)[R][NB], int kt) {
